@@ -1,0 +1,294 @@
+"""Plant plausible slips in the oracle (on the CPU) and check that a pin fails.
+
+Each mutant replaces one oracle function with a copy carrying a single slip
+(a dropped term, a flipped sign, a transposed operand, a wrong axis or
+comparison). The pins in ``test_oracle_pins.py`` must reject every mutant;
+that is what makes them pins rather than retypings of the oracle.
+"""
+import numpy as np
+import pytest
+
+import oracle.adamw as oadamw
+import oracle.muon as omuon
+import oracle.storage as ostorage
+from tests import test_oracle_pins as pins
+
+A, B, C = pins.A, pins.B, pins.C
+
+
+def _ns_template(M, steps=5, eps=1e-7, coeffs=(A, B, C), *, wrong_side=False,
+                 spectral=False, drop_eps=False, steps_delta=0):
+    X = np.array(M, dtype=np.float64)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    nrm = np.linalg.norm(X, 2) if spectral else np.linalg.norm(X)
+    X = X / (nrm + (0.0 if drop_eps else eps))
+    a, b, c = coeffs
+    for _ in range(steps + steps_delta):
+        Am = X @ X.T
+        Bm = b * Am + c * (Am @ Am)
+        X = a * X + (X.T @ Bm.T).T if wrong_side else a * X + Bm @ X
+    return X.T if tall else X
+
+
+def ns_flip_b(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+    return _ns_template(M, steps, eps, (A, -B, C))
+
+
+def ns_drop_c(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+    return _ns_template(M, steps, eps, (A, B, 0.0))
+
+
+def ns_spectral(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+    return _ns_template(M, steps, eps, coeffs, spectral=True)
+
+
+def ns_no_eps(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+    return _ns_template(M, steps, eps, coeffs, drop_eps=True)
+
+
+def ns_four_steps(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+    return _ns_template(M, steps, eps, coeffs, steps_delta=-1)
+
+
+def ns_xa_order(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+    """X (bA + cA^2) instead of (bA + cA^2) X: the operands swap places, which
+    only type-checks (and only differs) for a square matrix."""
+    X = np.array(M, dtype=np.float64)
+    tall = X.shape[0] > X.shape[1]
+    if tall:
+        X = X.T
+    X = X / (np.linalg.norm(X) + eps)
+    a, b, c = coeffs
+    for _ in range(steps):
+        Am = X @ X.T
+        Bm = b * Am + c * (Am @ Am)
+        X = a * X + (X @ Bm if X.shape[0] == X.shape[1] else Bm @ X)
+    return X.T if tall else X
+
+
+NS_MUTANTS = [ns_flip_b, ns_drop_c, ns_spectral, ns_no_eps, ns_four_steps, ns_xa_order]
+
+
+@pytest.mark.parametrize("mutant", NS_MUTANTS, ids=lambda f: f.__name__)
+def test_ns_mutants_caught(mutant, monkeypatch):
+    with pytest.raises(AssertionError):
+        pins.check_ns_svd(mutant)
+    monkeypatch.setattr(omuon, "newton_schulz", mutant)
+    with pytest.raises(AssertionError):
+        pins.check_first_step()
+
+
+def momentum_no_dampening(Bm, G, beta):
+    return beta * Bm + G
+
+
+def momentum_swapped(Bm, G, beta):
+    return (1.0 - beta) * Bm + beta * G
+
+
+def nesterov_old_sign(G, Bm, beta):
+    return G - beta * (Bm - G)
+
+
+def scale_swapped(m, n):
+    return max(1.0, n / m) ** 0.5
+
+
+def scale_no_sqrt(m, n):
+    return max(1.0, m / n)
+
+
+def decay_not_lr_scaled(W, U, lr, wd, s):
+    return (1.0 - wd) * W - lr * s * U
+
+
+def decay_dropped(W, U, lr, wd, s):
+    return W - lr * s * U
+
+
+@pytest.mark.parametrize("name,mutant", [
+    ("momentum_ema", momentum_no_dampening),
+    ("momentum_ema", momentum_swapped),
+    ("nesterov_lerp", nesterov_old_sign),
+    ("shape_scale", scale_swapped),
+    ("shape_scale", scale_no_sqrt),
+    ("apply_decoupled", decay_not_lr_scaled),
+    ("apply_decoupled", decay_dropped),
+], ids=lambda x: x if isinstance(x, str) else x.__name__)
+def test_step_mutants_caught(name, mutant, monkeypatch):
+    monkeypatch.setattr(omuon, name, mutant)
+    failures = 0
+    for check in (pins.check_first_step, pins.check_second_step, pins.check_views):
+        try:
+            check()
+        except AssertionError:
+            failures += 1
+    assert failures >= 1
+
+
+def test_nesterov_using_old_momentum_caught(monkeypatch):
+    """Nesterov from the momentum before this step's update."""
+    real = omuon.muon_tensor_step
+
+    def stale(W, G, Bm, V, views, hp, lr, wd):
+        beta = hp.get("beta", 0.95)
+        Q = G + beta * (Bm - G)
+        B_new = omuon.momentum_ema(Bm, G, beta)
+        Wn = np.empty_like(W)
+        m = W.shape[1] // views
+        for b in range(W.shape[0]):
+            for v in range(views):
+                sl = slice(v * m, (v + 1) * m)
+                Wn[b, sl], _, _ = omuon.matrix_update(Q[b, sl], W[b, sl], G[b, sl], None, hp, lr, wd)
+        return Wn, B_new, None, None
+
+    with pytest.raises(AssertionError):
+        pins.check_second_step(stale)
+    pins.check_second_step(real)
+
+
+def view_scale_from_parent(W, G, Bm, V, views, hp, lr, wd):
+    """Scale taken from the packed parent's rows instead of the view's."""
+    beta = hp.get("beta", 0.95)
+    B_new = omuon.momentum_ema(Bm, G, beta)
+    Q = omuon.nesterov_lerp(G, B_new, beta)
+    batch, rows, cols = W.shape
+    m = rows // views
+    Wn = np.empty_like(W)
+    for b in range(batch):
+        for v in range(views):
+            sl = slice(v * m, (v + 1) * m)
+            U = omuon.newton_schulz(Q[b, sl])
+            Wn[b, sl] = omuon.apply_decoupled(W[b, sl], U, lr, wd, omuon.shape_scale(rows, cols))
+    return Wn, B_new, None, None
+
+
+def whole_parent_ns(W, G, Bm, V, views, hp, lr, wd):
+    """The packed parent orthogonalised as one matrix (views ignored)."""
+    return omuon.muon_tensor_step(W, G, Bm, V, 1, hp, lr, wd)
+
+
+@pytest.mark.parametrize("mutant", [view_scale_from_parent, whole_parent_ns],
+                         ids=lambda f: f.__name__)
+def test_view_mutants_caught(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_views(mutant)
+
+
+def normuon_column_axis(U, V, beta2):
+    v_mean = np.mean(U * U, axis=0)
+    V_new = V + (1.0 - beta2) * (v_mean[: V.shape[0]] - V)
+    U_hat = U * (np.maximum(V_new, 1e-30) ** -0.5)[:, None]
+    return U_hat * (np.linalg.norm(U) / np.linalg.norm(U_hat)), V_new
+
+
+def normuon_not_norm_preserving(U, V, beta2):
+    v_mean = np.mean(U * U, axis=1)
+    V_new = V + (1.0 - beta2) * (v_mean - V)
+    return U * (np.maximum(V_new, 1e-30) ** -0.5)[:, None], V_new
+
+
+def normuon_beta_swapped(U, V, beta2):
+    v_mean = np.mean(U * U, axis=1)
+    V_new = V + beta2 * (v_mean - V)
+    U_hat = U * (np.maximum(V_new, 1e-30) ** -0.5)[:, None]
+    return U_hat * (np.linalg.norm(U) / np.linalg.norm(U_hat)), V_new
+
+
+@pytest.mark.parametrize("mutant", [normuon_column_axis, normuon_not_norm_preserving,
+                                    normuon_beta_swapped], ids=lambda f: f.__name__)
+def test_normuon_mutants_caught(mutant):
+    with pytest.raises((AssertionError, ValueError)):
+        pins.check_normuon(mutant)
+
+
+def muon_plus_columns_first(U, eps):
+    U = U / np.sqrt(np.sum(U * U, axis=0, keepdims=True) + eps)
+    return U / np.sqrt(np.sum(U * U, axis=1, keepdims=True) + eps)
+
+
+def muon_plus_eps_outside(U, eps):
+    U = U / (np.sqrt(np.sum(U * U, axis=1, keepdims=True)) + eps)
+    return U / (np.sqrt(np.sum(U * U, axis=0, keepdims=True)) + eps)
+
+
+@pytest.mark.parametrize("mutant", [muon_plus_columns_first, muon_plus_eps_outside],
+                         ids=lambda f: f.__name__)
+def test_muon_plus_mutants_caught(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_muon_plus(mutant)
+
+
+def wrapper_ge(W, U, G, lr, wd, s):
+    delta = lr * wd * W + lr * s * U
+    mask = (delta * G) >= 0.0
+    return np.where(mask, W - delta, W), mask
+
+
+def wrapper_no_decay(W, U, G, lr, wd, s):
+    delta = lr * s * U
+    mask = (delta * G) > 0.0
+    return np.where(mask, W - lr * wd * W - delta, W), mask
+
+
+def wdmask_strict(W, U, lr, wd, s):
+    mask = (U * W) > 0.0
+    return W - lr * s * U - lr * wd * np.where(mask, W, 0.0)
+
+
+def test_cautious_mutants_caught():
+    with pytest.raises(AssertionError):
+        pins.check_cautious(wrapper=wrapper_ge)
+    with pytest.raises(AssertionError):
+        pins.check_cautious(wrapper=wrapper_no_decay)
+    with pytest.raises(AssertionError):
+        pins.check_cautious(wdmask=wdmask_strict)
+
+
+def adamw_eps_inside(p, g, m, v, lr, wd, b1, b2, eps, step):
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh, vh = m / (1 - b1 ** step), v / (1 - b2 ** step)
+    return p - lr * (mh / np.sqrt(vh + eps) + wd * p), m, v
+
+
+def adamw_no_bias_correction(p, g, m, v, lr, wd, b1, b2, eps, step):
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    return p - lr * (m / (np.sqrt(v) + eps) + wd * p), m, v
+
+
+def adamw_coupled_decay(p, g, m, v, lr, wd, b1, b2, eps, step):
+    g = g + wd * p
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh, vh = m / (1 - b1 ** step), v / (1 - b2 ** step)
+    return p - lr * mh / (np.sqrt(vh) + eps), m, v
+
+
+@pytest.mark.parametrize("mutant", [adamw_eps_inside, adamw_no_bias_correction,
+                                    adamw_coupled_decay], ids=lambda f: f.__name__)
+def test_adamw_mutants_caught(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_adamw(mutant)
+
+
+def bf16_truncate(x):
+    x = np.asarray(x, dtype=np.float64)
+    return (x.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_via_f32(x):
+    """Double rounding through binary32: differs from one rounding near ties."""
+    x32 = np.asarray(x, dtype=np.float64).astype(np.float32)
+    u = x32.view(np.uint32).astype(np.uint64)
+    u = (u + 0x7FFF + ((u >> 16) & 1)) >> 16
+    return u.astype(np.uint16)
+
+
+@pytest.mark.parametrize("mutant", [bf16_truncate, bf16_via_f32], ids=lambda f: f.__name__)
+def test_bf16_rounding_mutants_caught(mutant):
+    with pytest.raises(AssertionError):
+        pins.check_bf16_rounding(mutant)

@@ -1,0 +1,433 @@
+"""Pins of the fp64 oracle against what the pages and the mathematics fix.
+
+CPU only. Each check is written so that a plausible slip in the oracle (a
+dropped term, a wrong sign or index, a transposed operand) fails at least one of
+them; ``test_oracle_mutations.py`` plants such slips and asserts they are
+caught. Expected values come from closed forms derived here, the SVD reduction
+of the Newton-Schulz iteration (a textbook identity computed with
+numpy.linalg.svd), invariants the pages state, and brute force on tiny inputs.
+"""
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import adamw as oadamw
+from oracle import muon as omuon
+from oracle import storage
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "page_constants.json")
+with open(GOLDEN) as f:
+    PAGE = json.load(f)
+A, B, C = PAGE["ns_coeffs"]["value"]
+STEPS = PAGE["ns_steps"]["value"]
+EPS = PAGE["ns_eps"]["value"]
+
+
+def rng(seed):
+    return np.random.default_rng(seed)
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz through the SVD: X = U S V^T  =>  X X^T = U S^2 U^T, and each
+# iteration maps every singular value x to phi(x) = a x + b x^3 + c x^5 while
+# keeping the singular vectors. This route shares nothing with the oracle's
+# matrix iteration.
+# ---------------------------------------------------------------------------
+def phi_iter(x, steps=STEPS, coeffs=(A, B, C)):
+    a, b, c = coeffs
+    for _ in range(steps):
+        x = a * x + b * x ** 3 + c * x ** 5
+    return x
+
+
+def ns_by_svd(X, steps=STEPS, eps=EPS):
+    U, S, Vt = np.linalg.svd(np.asarray(X, dtype=np.float64), full_matrices=False)
+    fro = math.sqrt(float(np.sum(S * S)))
+    return (U * phi_iter(S / (fro + eps), steps)) @ Vt
+
+
+def check_ns_svd(ns=None):
+    ns = ns or omuon.newton_schulz
+    r = rng(11)
+    for shape in [(4, 3), (3, 4), (5, 5), (6, 2), (2, 7), (1, 5), (8, 8)]:
+        X = r.standard_normal(shape)
+        got = ns(X)
+        want = ns_by_svd(X)
+        err = np.linalg.norm(got - want) / np.linalg.norm(want)
+        assert err < 1e-11, (shape, err)
+    # a small-norm input makes the eps term visible
+    X = 1e-4 * r.standard_normal((4, 3))
+    got, want = ns(X), ns_by_svd(X)
+    assert np.linalg.norm(got - want) / np.linalg.norm(want) < 1e-11
+
+
+def test_ns_matches_svd_reduction():
+    check_ns_svd()
+
+
+def test_ns_scalar_constants():
+    # rank-1 input: the single normalised singular value is 1/(1+eps/||X||) ~ 1
+    assert abs(phi_iter(1.0) - 0.6964364094697522) < 1e-15
+    u = rng(1).standard_normal(6)
+    v = rng(2).standard_normal(4)
+    X = np.outer(u, v)
+    got = omuon.newton_schulz(X)
+    nrm = np.linalg.norm(X)
+    want = phi_iter(nrm / (nrm + EPS)) * X / nrm
+    assert np.abs(got - want).max() < 1e-13
+    # 4x3 with orthonormal columns: every normalised singular value is 1/sqrt(3)
+    Q, _ = np.linalg.qr(rng(3).standard_normal((4, 3)))
+    got = omuon.newton_schulz(Q)
+    f = phi_iter((1 / math.sqrt(3)) * math.sqrt(3) / (math.sqrt(3) + EPS))
+    assert abs(f - 0.6857849207555402) < 1e-6
+    assert np.abs(got - f * Q).max() < 1e-13
+
+
+def test_ns_transpose_symmetry():
+    r = rng(5)
+    for shape in [(7, 3), (3, 7), (16, 48)]:
+        X = r.standard_normal(shape)
+        assert np.array_equal(omuon.newton_schulz(X.T), omuon.newton_schulz(X).T)
+    X = r.standard_normal((9, 9))
+    d = np.abs(omuon.newton_schulz(X.T) - omuon.newton_schulz(X).T).max()
+    assert d < 1e-13
+
+
+def test_ns_zero_stays_finite():
+    for shape in [(4, 3), (3, 4), (16, 16)]:
+        out = omuon.newton_schulz(np.zeros(shape))
+        assert np.all(np.isfinite(out)) and np.all(out == 0.0)
+
+
+def test_ns_output_band():
+    # well-conditioned inputs: normalised singular values >= 1.5e-3 land in
+    # phi^5's band; the band's ends are checked on a dense grid first
+    grid = np.linspace(1.5e-3, 1.0, 200001)
+    y = phi_iter(grid)
+    assert y.min() > 0.679 and y.max() < 1.2025
+    r = rng(7)
+    U, _ = np.linalg.qr(r.standard_normal((256, 128)))
+    V, _ = np.linalg.qr(r.standard_normal((128, 128)))
+    S = np.geomspace(1.0, 0.1, 128)          # condition number 10
+    X = (U * S) @ V.T
+    sv = np.linalg.svd(omuon.newton_schulz(X), compute_uv=False)
+    assert sv.min() > 0.679 and sv.max() < 1.2025
+    G = r.standard_normal((96, 384))           # Gaussian, aspect 4: well conditioned
+    sv = np.linalg.svd(omuon.newton_schulz(G), compute_uv=False)
+    assert sv.min() > 0.679 and sv.max() < 1.2025
+
+
+# ---------------------------------------------------------------------------
+# Whole-matrix closed forms from zero momentum (beta 0.95, lr 0.02, wd 0.1)
+# ---------------------------------------------------------------------------
+HP = {"beta": 0.95, "nesterov": True}
+
+
+def check_first_step(step_fn=None):
+    step_fn = step_fn or omuon.muon_tensor_step
+    r = rng(0)
+    for (m, n, s) in [(256, 128, math.sqrt(2.0)), (64, 96, 1.0), (96, 64, math.sqrt(1.5)),
+                      (40, 40, 1.0)]:
+        G = r.standard_normal((1, m, n))
+        W = 0.02 * r.standard_normal((1, m, n))
+        Bm = np.zeros((1, m, n))
+        W1, B1, _, _ = step_fn(W, G, Bm, None, 1, HP, 0.02, 0.1)
+        assert np.abs(B1 - 0.05 * G).max() <= 1e-16 * np.abs(G).max() * 4
+        U = ns_by_svd(0.0975 * G[0])
+        want = 0.998 * W[0] - 0.02 * s * U
+        err = np.abs(W1[0] - want).max()
+        assert err < 1e-14, (m, n, err)
+
+
+def test_first_step_closed_form():
+    check_first_step()
+
+
+def check_second_step(step_fn=None):
+    step_fn = step_fn or omuon.muon_tensor_step
+    r = rng(1)
+    m, n = 48, 80
+    G1 = r.standard_normal((1, m, n))
+    G2 = r.standard_normal((1, m, n))
+    W0 = 0.02 * r.standard_normal((1, m, n))
+    W1, B1, _, _ = step_fn(W0, G1, np.zeros((1, m, n)), None, 1, HP, 0.02, 0.1)
+    W2, B2, _, _ = step_fn(W1, G2, B1, None, 1, HP, 0.02, 0.1)
+    assert np.abs(B2 - (0.0475 * G1 + 0.05 * G2)).max() < 1e-15
+    Q2 = 0.045125 * G1[0] + 0.0975 * G2[0]
+    want = 0.998 * W1[0] - 0.02 * ns_by_svd(Q2)
+    assert np.abs(W2[0] - want).max() < 1e-14
+
+
+def test_second_step_closed_form():
+    check_second_step()
+
+
+def test_nesterov_off_uses_momentum():
+    r = rng(2)
+    G = r.standard_normal((1, 8, 12))
+    B0 = r.standard_normal((1, 8, 12))
+    W = np.zeros((1, 8, 12))
+    hp = {"beta": 0.9, "nesterov": False}
+    W1, B1, _, _ = omuon.muon_tensor_step(W, G, B0, None, 1, hp, 0.5, 0.0)
+    assert np.allclose(B1, 0.9 * B0 + 0.1 * G, rtol=0, atol=1e-15)
+    assert np.abs(W1[0] + 0.5 * ns_by_svd(B1[0])).max() < 1e-14
+
+
+def check_views(step_fn=None):
+    """A (2, m, n) view: each half is its own matrix with its own scale."""
+    step_fn = step_fn or omuon.muon_tensor_step
+    r = rng(3)
+    m, n = 8, 4                       # each view is tall 8x4 -> scale sqrt(2)
+    G = r.standard_normal((1, 2 * m, n))
+    W = 0.02 * r.standard_normal((1, 2 * m, n))
+    W1, _, _, _ = step_fn(W, G, np.zeros_like(G), None, 2, HP, 0.02, 0.1)
+    for v in range(2):
+        sl = slice(v * m, (v + 1) * m)
+        want = 0.998 * W[0, sl] - 0.02 * math.sqrt(2.0) * ns_by_svd(0.0975 * G[0, sl])
+        assert np.abs(W1[0, sl] - want).max() < 1e-14
+
+
+def test_views_are_independent_matrices():
+    check_views()
+
+
+def test_batch_entries_are_independent():
+    r = rng(4)
+    G = r.standard_normal((3, 6, 10))
+    W = r.standard_normal((3, 6, 10))
+    W1, _, _, _ = omuon.muon_tensor_step(W, G, np.zeros_like(G), None, 1, HP, 0.02, 0.1)
+    for b in range(3):
+        Wb, _, _, _ = omuon.muon_tensor_step(W[b:b + 1], G[b:b + 1], np.zeros_like(G[b:b + 1]),
+                                             None, 1, HP, 0.02, 0.1)
+        assert np.array_equal(Wb[0], W1[b])
+
+
+def test_absent_gradient_leaves_everything():
+    W = rng(5).standard_normal((2, 4, 4))
+    Bm = rng(6).standard_normal((2, 4, 4))
+    V = np.abs(rng(7).standard_normal((2, 4)))
+    W1, B1, V1, U = omuon.muon_tensor_step(W, None, Bm, V, 1, {"normuon": True}, 0.02, 0.1)
+    assert np.array_equal(W1, W) and np.array_equal(B1, Bm) and np.array_equal(V1, V)
+    assert U is None
+
+
+def test_zero_gradient_only_decays():
+    W = rng(8).standard_normal((1, 5, 7))
+    W1, B1, _, _ = omuon.muon_tensor_step(W, np.zeros_like(W), np.zeros_like(W), None, 1,
+                                          HP, 0.02, 0.1)
+    assert np.all(np.isfinite(W1)) and np.all(B1 == 0.0)
+    assert np.array_equal(W1, 0.998 * W)
+
+
+def test_shape_scale_values():
+    assert omuon.shape_scale(256, 128) == math.sqrt(2.0)
+    assert omuon.shape_scale(3072, 768) == 2.0
+    assert abs(omuon.shape_scale(14336, 4096) - 1.8708286933869707) < 1e-15
+    assert abs(omuon.shape_scale(28672, 8192) - 1.8708286933869707) < 1e-15
+    assert omuon.shape_scale(768, 3072) == 1.0
+    assert omuon.shape_scale(768, 768) == 1.0
+
+
+# ---------------------------------------------------------------------------
+# NorMuon, Muon+ and the cautious masks
+# ---------------------------------------------------------------------------
+def check_normuon(fn=None):
+    fn = fn or omuon.normuon
+    r = rng(9)
+    m, n = 12, 20
+    U = r.standard_normal((m, n)) * np.linspace(0.2, 3.0, m)[:, None]
+    out, V1 = fn(U, np.zeros(m), 0.95)
+    # step 1 from zero state: V = 0.05 * row mean of U^2 and every output row
+    # has the same norm, ||U||_F / sqrt(m); directions are kept row by row
+    assert np.abs(V1 - 0.05 * (U * U).sum(axis=1) / n).max() < 1e-15
+    rn = np.linalg.norm(out, axis=1)
+    assert np.abs(rn - np.linalg.norm(U) / math.sqrt(m)).max() < 1e-12
+    assert abs(np.linalg.norm(out) - np.linalg.norm(U)) < 1e-12
+    cos = (out * U).sum(axis=1) / (rn * np.linalg.norm(U, axis=1))
+    assert np.abs(cos - 1.0).max() < 1e-14
+    # step 2: V2 = 0.95 V1 + 0.05 rho2
+    U2 = r.standard_normal((m, n))
+    _, V2 = fn(U2, V1, 0.95)
+    assert np.abs(V2 - (0.95 * V1 + 0.05 * (U2 * U2).sum(axis=1) / n)).max() < 1e-15
+
+
+def test_normuon_rows():
+    check_normuon()
+
+
+def check_muon_plus(fn=None):
+    fn = fn or omuon.muon_plus_row_col
+    r = rng(10)
+    U = r.standard_normal((9, 14)) * np.linspace(0.1, 2.0, 14)[None, :]
+    out = fn(U, 0.0)
+    # rows are normalised first, columns last: with eps 0 the columns are unit
+    assert np.abs(np.linalg.norm(out, axis=0) - 1.0).max() < 1e-14
+    # the row stage leaves each column's entries in the ratio U_ij / ||U_i||
+    R = U / np.linalg.norm(U, axis=1, keepdims=True)
+    assert np.abs(out - R / np.linalg.norm(R, axis=0, keepdims=True)).max() < 1e-14
+    # scaled orthogonal matrix: every row and column has norm t
+    Q, _ = np.linalg.qr(r.standard_normal((6, 6)))
+    t, eps = 0.3, 1e-8
+    out = fn(t * Q, eps)
+    k = 1.0 / (math.sqrt(t * t + eps) * math.sqrt(t * t / (t * t + eps) + eps))
+    assert np.abs(out - k * t * Q).max() < 1e-15
+
+
+def test_muon_plus_row_col():
+    check_muon_plus()
+
+
+def check_cautious(wrapper=None, wdmask=None):
+    wrapper = wrapper or omuon.apply_cautious_wrapper
+    wdmask = wdmask or omuon.apply_cautious_wd
+    r = rng(12)
+    W = r.standard_normal((6, 8))
+    U = r.standard_normal((6, 8))
+    G = r.standard_normal((6, 8))
+    lr, wd, s = 0.02, 0.1, 1.5
+    # ties: a zero gradient entry and a zero update entry keep the old value
+    G[0, 0] = 0.0
+    W[1, 1] = 0.0
+    U[1, 1] = 0.0
+    out, mask = wrapper(W, U, G, lr, wd, s)
+    delta = lr * wd * W + lr * s * U
+    keep = ~((delta * G) > 0)
+    assert keep[0, 0] and keep[1, 1]
+    assert np.array_equal(out[keep], W[keep])
+    assert np.array_equal(out[~keep], (W - delta)[~keep])
+    assert np.array_equal(mask, ~keep)
+    # weight-decay mask: no decay where U*W < 0; a zero product still decays
+    out = wdmask(W, U, lr, wd, s)
+    neg = (U * W) < 0
+    assert np.array_equal(out[neg], (W - lr * s * U)[neg])
+    assert np.array_equal(out[~neg], (W - lr * s * U - lr * wd * W)[~neg])
+    W2 = W.copy()
+    W2[2, 2] = 0.0
+    U2 = U.copy()
+    U2[3, 3] = 0.0
+    o2 = wdmask(W2, U2, lr, wd, s)
+    assert o2[3, 3] == W2[3, 3] - lr * wd * W2[3, 3]
+
+
+def test_cautious_masks():
+    check_cautious()
+
+
+def test_step_with_normuon_and_cautious_wd():
+    """Config-4-like tensor (2 views, batch 2): the full step equals NS by SVD,
+    then NorMuon's closed form, then the masked apply, matrix by matrix."""
+    r = rng(13)
+    batch, views, m, n = 2, 2, 6, 10
+    G = r.standard_normal((batch, views * m, n))
+    W = 0.02 * r.standard_normal((batch, views * m, n))
+    V = np.zeros((batch, views * m))
+    hp = dict(HP, normuon=True, normuon_beta2=0.95, cautious="wd_mask")
+    W1, _, V1, _ = omuon.muon_tensor_step(W, G, np.zeros_like(G), V, views, hp, 0.02, 0.1)
+    for b in range(batch):
+        for v in range(views):
+            sl = slice(v * m, (v + 1) * m)
+            U = ns_by_svd(0.0975 * G[b, sl])
+            Vv = 0.05 * (U * U).mean(axis=1)
+            assert np.abs(V1[b, sl] - Vv).max() < 1e-15
+            Un = U / np.sqrt(Vv)[:, None]
+            Un *= np.linalg.norm(U) / np.linalg.norm(Un)
+            Wv = W[b, sl]
+            decay = np.where(Un * Wv >= 0, Wv, 0.0)
+            want = Wv - 0.02 * Un - 0.02 * 0.1 * decay
+            assert np.abs(W1[b, sl] - want).max() < 1e-14
+
+
+# ---------------------------------------------------------------------------
+# AdamW closed forms
+# ---------------------------------------------------------------------------
+def check_adamw(fn=None):
+    fn = fn or oadamw.adamw_update
+    r = rng(14)
+    p0 = 0.02 * r.standard_normal(1000)
+    g1 = 1e-3 * r.standard_normal(1000)
+    g2 = 1e-3 * r.standard_normal(1000)
+    lr, wd, eps = 3e-4, 0.1, 1e-8
+    p1, m1, v1 = fn(p0, g1, np.zeros(1000), np.zeros(1000), lr, wd, 0.9, 0.95, eps, 1)
+    def rel(x, y):
+        return np.abs(x - y).max() / np.abs(y).max()
+    assert rel(m1, 0.1 * g1) < 1e-15
+    assert rel(v1, 0.05 * g1 * g1) < 1e-15
+    want1 = p0 - lr * (g1 / (np.abs(g1) + eps) + wd * p0)
+    assert rel(p1, want1) < 1e-15
+    p2, m2, v2 = fn(p1, g2, m1, v1, lr, wd, 0.9, 0.95, eps, 2)
+    mm = 0.09 * g1 + 0.1 * g2
+    vv = 0.0475 * g1 * g1 + 0.05 * g2 * g2
+    want2 = p1 - lr * ((mm / 0.19) / (np.sqrt(vv / 0.0975) + eps) + wd * p1)
+    assert rel(m2, mm) < 1e-15
+    assert rel(v2, vv) < 1e-15
+    assert rel(p2, want2) < 1e-15
+
+
+def test_adamw_closed_forms():
+    check_adamw()
+
+
+def test_adamw_zero_grad_is_pure_decay():
+    p = np.linspace(-1, 1, 11)
+    p1, m1, v1 = oadamw.adamw_update(p, np.zeros(11), np.zeros(11), np.zeros(11),
+                                     1e-3, 0.1, 0.9, 0.95, 1e-8, 1)
+    assert np.array_equal(m1, np.zeros(11)) and np.array_equal(v1, np.zeros(11))
+    assert np.allclose(p1, p * (1 - 1e-4), rtol=0, atol=1e-18)
+
+
+# ---------------------------------------------------------------------------
+# Storage formats
+# ---------------------------------------------------------------------------
+def check_bf16_rounding(fn=None):
+    fn = fn or storage.round_bf16_bits
+    cases = {1.0: 0x3F80, -2.5: 0xC020, 1.0 + 2 ** -8: 0x3F80, 1.0 + 3 * 2 ** -8: 0x3F82,
+             1.0 + 2 ** -8 + 2 ** -30: 0x3F81, 0.0: 0x0000, 2 ** -133: 0x0001,
+             3.0e38: 0x7F62}
+    for x, bits in cases.items():
+        assert int(fn(np.array([x]))[0]) == bits, (x, hex(int(fn(np.array([x]))[0])))
+    assert int(fn(np.array([np.nan]))[0]) & 0x7F80 == 0x7F80
+    # values exact in binary32 round the same as torch's float32 -> bfloat16
+    x = (np.random.default_rng(15).standard_normal(100000) * 10.0 ** np.random.default_rng(16)
+         .integers(-20, 20, 100000)).astype(np.float32)
+    ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(fn(x.astype(np.float64)), ref)
+
+
+def test_bf16_rounding():
+    check_bf16_rounding()
+
+
+def test_decode():
+    bits = np.array([0x3F80, 0xC020, 0x0001, 0x7F80], dtype=np.uint16)
+    v = storage.decode(bits, "bf16")
+    assert v[0] == 1.0 and v[1] == -2.5 and v[2] == 2.0 ** -133 and np.isinf(v[3])
+    f = np.array([1.5, -3.25], dtype=np.float32)
+    assert np.array_equal(storage.decode(f, "f32"), np.array([1.5, -3.25]))
+
+
+def test_round_trip_f32_state():
+    x = np.random.default_rng(17).standard_normal(1000)
+    assert np.array_equal(storage.round_f32(x), x.astype(np.float32))
+
+
+def test_muon_step_dict_api_bf16():
+    """The list-of-tensors entry with bf16 storage: outputs round once from fp64."""
+    r = rng(18)
+    W = (0.02 * r.standard_normal((1, 16, 8))).astype(np.float32)
+    G = r.standard_normal((1, 16, 8)).astype(np.float32)
+    Wb = torch.from_numpy(W).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    Gb = torch.from_numpy(G).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    t = {"param": Wb, "param_dtype": "bf16", "grad": Gb, "grad_dtype": "bf16",
+         "momentum": np.zeros((1, 16, 8), np.float32), "row_v": None, "views": 1,
+         "lr": 0.02, "wd": 0.1, "shape": (1, 16, 8)}
+    out = omuon.muon_step([t], HP)[0]
+    W64 = storage.decode(Wb, "bf16")
+    G64 = storage.decode(Gb, "bf16")
+    want = 0.998 * W64[0] - 0.02 * math.sqrt(2.0) * ns_by_svd(0.0975 * G64[0])
+    assert np.abs(out["W64"][0] - want).max() < 1e-14
+    assert np.array_equal(out["param"], storage.round_bf16_bits(out["W64"]))
+    assert np.array_equal(out["momentum"], (0.05 * G64).astype(np.float32))
