@@ -1,0 +1,245 @@
+"""Benchmark of the hybrid Muon + AdamW step on one MI355X.
+
+Default workload: the GPT-style 12-layer d=768 parameter set (72 Muon
+matrices: Q, K, V, O 768x768, MLP up 3072x768 and down 768x3072, fp32 storage,
+bf16 Newton-Schulz; AdamW on the tied 50304x768 embedding and 25 RMSNorm
+weights). A step is one muon_step plus one adamw_step over the whole set, with
+every input already resident in HBM. Prints one JSON line.
+
+The Newton-Schulz figures use algorithmic FLOPs of what is computed: per
+iteration r(r+1)c for the Gram (one triangle), r(r+1)r for A^2 (one triangle)
+and 2r^2c for B X, per canonical r x c matrix.
+"""
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, HERE)
+
+BF16_PEAK_TFLOPS = 2516.6     # 256 CU x 4096 flop/clk x 2.4 GHz, dense
+HBM_PEAK_GBPS = 8000.0
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", type=int, default=2, help="parameter set 1-5 (default 2)")
+    ap.add_argument("--profile-steps", type=int, default=5)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
+    ap.add_argument("--calib-copy", action="store_true",
+                    help="also run a plain 1 GiB device copy (counter calibration)")
+    return ap.parse_args()
+
+
+def ns_flops(r, c, steps):
+    return steps * (r * (r + 1) * c + r * (r + 1) * r + 2 * r * r * c)
+
+
+def ns_flops_per_launch(mats):
+    """Algorithmic FLOPs of one launch of each Newton-Schulz product."""
+    gram = sum(r * (r + 1) * c for r, c in mats)
+    square = sum(r * (r + 1) * r for r, c in mats)
+    apply = sum(2 * r * r * c for r, c in mats)
+    return {"ns_gram_bf16": gram, "ns_square_bf16": square, "ns_apply_bf16": apply,
+            "ns_gram_f32": gram, "ns_square_f32": square, "ns_apply_f32": apply}
+
+
+def elementwise_bytes(wl):
+    """Algorithmic HBM bytes of one launch of each elementwise kernel."""
+    es = {"f32": 4, "bf16": 2}
+    nsb = es[wl.muon_hp.ns_dtype]
+    mom = 0
+    app = 0
+    for t in wl.muon:
+        if not t.has_grad:
+            continue
+        n = t.numel
+        mom += n * (es[t.grad_dtype] + 4 + 4 + nsb)
+        app += n * (2 * es[t.param_dtype] + nsb + (es[t.grad_dtype] if wl.muon_hp.cautious == "wrapper" else 0))
+    adam = sum(t.numel * (2 * es[t.param_dtype] + es[t.grad_dtype] + 16) for t in wl.adamw)
+    return {"momentum": mom, "apply_update": app, "adamw": adam}
+
+
+def cpu_baseline(wl, data, budget_s):
+    """The fp64 oracle, untuned, on a bounded sample of the same workload:
+    whole Muon updates of the first matrices in tensor order until the time
+    budget is spent. Reported in the same unit as the GPU figure."""
+    import numpy as np
+    from oracle import muon as omuon
+    from workloads import to_numpy
+    from oracle import storage
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+    except Exception:  # pragma: no cover
+        threads = os.cpu_count()
+    h = wl.muon_hp
+    hp = {"beta": h.beta, "nesterov": h.nesterov, "ns_steps": h.ns_steps, "ns_coeffs": h.ns_coeffs,
+          "ns_eps": h.ns_eps, "normuon": h.normuon, "normuon_beta2": h.normuon_beta2,
+          "muon_plus": h.muon_plus, "muon_plus_eps": h.muon_plus_eps, "cautious": h.cautious}
+    flops = 0
+    nmat = 0
+    spent = 0.0
+    for t in data.muon:
+        if t is None or t.grad is None:
+            continue
+        inp = {"param": to_numpy(t.param), "param_dtype": t.spec.param_dtype, "grad": to_numpy(t.grad),
+               "grad_dtype": t.spec.grad_dtype, "momentum": to_numpy(t.momentum),
+               "row_v": None if t.row_v is None else to_numpy(t.row_v), "views": t.spec.views,
+               "lr": t.spec.lr, "wd": t.spec.wd, "shape": t.spec.shape}
+        t0 = time.perf_counter()
+        omuon.muon_step([inp], hp)
+        spent += time.perf_counter() - t0
+        for (_, _, m, n) in t.spec.matrices():
+            flops += ns_flops(min(m, n), max(m, n), h.ns_steps)
+            nmat += 1
+        if spent >= budget_s:
+            break
+    total = len(wl.matrices())
+    return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
+            "sample": f"full fp64 Muon update of {nmat} of {total} matrices ({spent:.1f} s)",
+            "matrices_per_s": nmat / spent}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
+              "(the multi-GPU sharding is a design, not an implementation).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    import muon_adamw_amd as ma
+    import workloads
+
+    if not torch.cuda.is_available():
+        print("no GPU visible", file=sys.stderr)
+        sys.exit(1)
+    wl = workloads.workload(args.config)
+    dev = "cuda"
+    t0 = time.time()
+    data = workloads.generate(wl, device=dev)
+    print(f"# generated {wl.name} in {time.time() - t0:.1f} s", file=sys.stderr, flush=True)
+    h = wl.muon_hp
+    hp = ma.muon_hparams(h.beta, h.nesterov, h.ns_steps, h.ns_coeffs, h.ns_eps, h.ns_dtype, h.normuon,
+                         h.normuon_beta2, h.muon_plus, h.muon_plus_eps, h.cautious)
+    mparams = [ma.MuonParam(t.param, t.grad, t.momentum, t.row_v, t.spec.views, t.spec.lr, t.spec.wd)
+               for t in data.muon]
+    aparams = [ma.AdamWParam(t.param, t.grad, t.m, t.v, t.spec.lr, t.spec.wd) for t in data.adamw]
+    ah = wl.adamw_hp
+    ws = torch.empty(ma.muon_workspace_bytes(mparams, hp), dtype=torch.uint8, device=dev)
+    cpu = None
+    if not args.no_cpu_baseline:
+        # the oracle reads the pre-step state, so time it before the GPU steps
+        cpu = cpu_baseline(wl, data, args.cpu_budget)
+        print(f"# cpu baseline: {cpu['sample']}", file=sys.stderr, flush=True)
+
+    stream = torch.cuda.current_stream()
+    step_no = [ah.step]
+
+    def hybrid_step(ev=None):
+        if ev is not None:
+            ev[0].record(stream)
+        ma.muon_step(mparams, hp, ws, stream)
+        if ev is not None:
+            ev[1].record(stream)
+        if aparams:
+            ma.adamw_step(aparams, ah.beta1, ah.beta2, ah.eps, step_no[0], stream)
+            step_no[0] += 1
+        if ev is not None:
+            ev[2].record(stream)
+
+    for _ in range(args.warmup):
+        hybrid_step()
+    torch.cuda.synchronize()
+
+    # whole-step timing
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        hybrid_step()
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t_start) / args.steps
+
+    # muon / adamw split with events on the step stream
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
+    for e in evs:
+        hybrid_step(e)
+    torch.cuda.synchronize()
+    muon_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
+    adam_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+
+    # per-kernel HIP-event timing (separate pass: events add gaps)
+    ma.profile_begin()
+    for _ in range(args.profile_steps):
+        hybrid_step()
+    prof = ma.profile_end()
+
+    if args.calib_copy:
+        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        del a, b
+
+    mats = [(min(m, n), max(m, n)) for (_, _, _, m, n) in wl.matrices()]
+    fl = ns_flops_per_launch(mats)
+    ns_total_flops = sum(ns_flops(r, c, h.ns_steps) for r, c in mats)
+    by = elementwise_bytes(wl)
+    kernels = {}
+    for name, (launches, total_ms) in prof.items():
+        avg_s = total_ms / launches / 1e3
+        k = {"launches_per_step": launches / args.profile_steps, "avg_us": avg_s * 1e6}
+        if name in fl:
+            ach = fl[name] / avg_s / 1e12
+            peak = BF16_PEAK_TFLOPS if name.endswith("bf16") else 157.3
+            k.update(bound="mfma" if name.endswith("bf16") else "alu", achieved=ach, peak=peak,
+                     unit="TFLOP/s", frac=ach / peak)
+        elif name in by:
+            ach = by[name] / avg_s / 1e9
+            k.update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s", frac=ach / HBM_PEAK_GBPS)
+        kernels[name] = k
+    ns_kernel_s = sum(prof[n][1] for n in prof if n.startswith("ns_")) / args.profile_steps / 1e3
+    dominant = max(prof, key=lambda n: prof[n][1])
+    dk = kernels[dominant]
+    roofline = {"bound": dk.get("bound"), "achieved": dk.get("achieved"), "peak": dk.get("peak"),
+                "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": None, "kernel": dominant}
+    muon_s = muon_ms / 1e3
+    value = ns_total_flops / muon_s / 1e12
+    line = {
+        "metric": "Muon step time & NS TFLOP/s (% bf16 MFMA peak); AdamW GB/s, 1 GPU",
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": h.ns_dtype if h.ns_dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "muon_matrices": len(mats),
+                   "adamw_elements": sum(t.numel for t in wl.adamw), "ns_steps": h.ns_steps,
+                   "parallelism": "none (1 GPU)"},
+        "muon_step_ms": round(muon_ms, 4),
+        "adamw_step_ms": round(adam_ms, 4),
+        "matrices_per_s": round(len(mats) / muon_s, 1),
+        "ns_tflops_kernels": round(ns_total_flops / ns_kernel_s / 1e12, 3),
+        "ns_frac_of_bf16_peak": round(ns_total_flops / ns_kernel_s / 1e12 / BF16_PEAK_TFLOPS, 4),
+        "adamw_GBps": round(by["adamw"] / (adam_ms / 1e3) / 1e9, 1) if aparams else None,
+        "roofline": roofline,
+        "kernels": kernels,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+
+
+if __name__ == "__main__":
+    main()

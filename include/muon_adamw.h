@@ -1,0 +1,255 @@
+/*
+ * muon_adamw.h -- C ABI of the MI355X (gfx950) hybrid Muon + AdamW step.
+ *
+ * Everything here is plain C: pointers, sizes and small structs. Device
+ * pointers address HBM on the GPU that is current when the call is made;
+ * host pointers are marked as such. No call allocates device memory: the
+ * caller owns every device buffer, including the Muon workspace. The library
+ * owns only small pinned host staging buffers for its launch tables.
+ *
+ * Errors: every entry point validates all of its arguments before it enqueues
+ * anything, so a non-OK status leaves every buffer untouched (the hybrid step
+ * is all-or-nothing, as the kimi-k3 "Optimization" chapter requires when an
+ * FP16 overflow skips "the whole hybrid optimizer update"). ma_last_error()
+ * returns a thread-local message for the last non-OK status. Kernel faults are
+ * asynchronous and surface at the caller's next synchronisation; a launch
+ * failure seen right after enqueueing returns MA_E_HIP.
+ *
+ * Streams: `stream` is a hipStream_t (NULL = the legacy default stream). All
+ * work of one call is enqueued on that stream in order; no call synchronises
+ * the host with the device except the staging ring's reuse wait (an event from
+ * four calls earlier). Calls that share a workspace must be ordered on one
+ * stream.
+ */
+#ifndef MUON_ADAMW_H
+#define MUON_ADAMW_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MA_OK = 0,
+  MA_E_INVALID = 1,      /* bad pointer, shape, flag or hyperparameter       */
+  MA_E_DTYPE = 2,        /* dtype outside {f32, bf16} (complex included)      */
+  MA_E_ALIAS = 3,        /* two tensors' parameter or state ranges overlap    */
+  MA_E_WORKSPACE = 4,    /* workspace missing or smaller than required        */
+  MA_E_UNSUPPORTED = 5,  /* a combination this library does not define        */
+  MA_E_HIP = 6           /* the HIP runtime reported an error                 */
+} ma_status;
+
+typedef enum { MA_F32 = 0, MA_BF16 = 1 } ma_dtype;
+
+typedef enum {
+  MA_CAUTIOUS_NONE = 0,
+  /* flaxchat "Optimizer" page, "Muon Algorithm" step 4: weight decay only
+   * where (update * param) >= 0; the orthogonalised update always applies. */
+  MA_CAUTIOUS_WD_MASK = 1,
+  /* speedtronic "v2 optimizers" page, "Cautious updates": keep an entry's
+   * whole observed update (decay included) only where update * grad > 0,
+   * otherwise leave the parameter unchanged. */
+  MA_CAUTIOUS_WRAPPER = 2
+} ma_cautious;
+
+/*
+ * One parameter tensor stepped by Muon (speedtronic "v2 optimizers" page,
+ * "Muon update"; kimi-k3 "Optimization", matrix views).
+ *
+ * param     device, batch*rows*cols elements of param_dtype, row-major and
+ *           contiguous: entry b is a rows x cols matrix (rows = output
+ *           features, cols = input features). Updated in place.
+ * grad      device, same shape, grad_dtype, read only. NULL means the tensor
+ *           has no gradient this step: nothing about it is read or written
+ *           (an inactive expert is neither moved nor decayed).
+ * momentum  device, fp32, same shape as param, updated in place. It belongs to
+ *           the packed parent: views share it, nothing is duplicated.
+ * row_v     device, fp32, batch*rows entries (one per stored row of each view),
+ *           updated in place; the NorMuon second moment (flaxchat "Muon
+ *           Algorithm" step 3). Required iff hparams.normuon, else ignored.
+ * views     rows are split into `views` equal blocks of rows/views rows; each
+ *           block of each batch entry is one independent matrix (a packed
+ *           gate/up is registered as (2, rows, columns)). rows % views == 0.
+ * lr, weight_decay  this tensor's learning rate and decoupled decay.
+ *
+ * Tied weights must be passed once: overlapping param or momentum ranges are
+ * rejected with MA_E_ALIAS.
+ */
+typedef struct {
+  void* param;
+  const void* grad;
+  float* momentum;
+  float* row_v;
+  int64_t batch;
+  int64_t rows;
+  int64_t cols;
+  int32_t views;
+  int32_t param_dtype;   /* ma_dtype */
+  int32_t grad_dtype;    /* ma_dtype */
+  float lr;
+  float weight_decay;
+} ma_muon_tensor;
+
+/*
+ * Hyperparameters shared by every Muon tensor of one call.
+ *
+ * beta, nesterov   B <- beta*B + (1-beta)*G; Q <- lerp(G, B, beta) if nesterov,
+ *                  else Q <- B (speedtronic "Muon update"; flaxchat step 1).
+ * ns_steps, ns_a, ns_b, ns_c, ns_eps
+ *                  X <- Q/(||Q||_F + ns_eps), then ns_steps times
+ *                  A = X X^T; X <- a X + (b A + c A^2) X, with a matrix that has
+ *                  more rows than columns transposed first and back after
+ *                  (speedtronic "Newton-Schulz": 5 steps, (3.4445, -4.7750,
+ *                  2.0315), eps 1e-7). 1 <= ns_steps <= 64.
+ * ns_dtype         MA_BF16: bf16 operands on the MFMA matrix cores with fp32
+ *                  accumulation; MA_F32: fp32 throughout.
+ * normuon, normuon_beta2
+ *                  NorMuon after Newton-Schulz: per stored row,
+ *                  V <- V + (1-beta2)(mean_j U_ij^2 - V); U_i <- U_i / sqrt(V_i),
+ *                  then rescaled to keep ||U||_F (flaxchat step 3).
+ * muon_plus, muon_plus_eps
+ *                  Muon+ row_col after Newton-Schulz: rows, then columns, to
+ *                  unit L2 norm with eps inside each square root (speedtronic
+ *                  "Muon+"). normuon and muon_plus together: MA_E_UNSUPPORTED.
+ * cautious         ma_cautious.
+ * After these, W <- (1 - lr*wd) W - lr * sqrt(max(1, m/n)) * U with m x n the
+ * view's stored shape, subject to the cautious mask.
+ */
+typedef struct {
+  float beta;
+  int32_t nesterov;
+  int32_t ns_steps;
+  float ns_a;
+  float ns_b;
+  float ns_c;
+  float ns_eps;
+  int32_t ns_dtype;
+  int32_t normuon;
+  float normuon_beta2;
+  int32_t muon_plus;
+  float muon_plus_eps;
+  int32_t cautious;
+} ma_muon_hparams;
+
+/* Device bytes of workspace muon_step needs for this tensor list (host call,
+ * no GPU work). Returns 0 and sets ma_last_error() if the arguments are
+ * invalid. */
+size_t ma_muon_workspace_bytes(const ma_muon_tensor* tensors, int32_t n,
+                               const ma_muon_hparams* hp);
+
+/*
+ * The Muon half of the hybrid step over `n` tensors (host array `tensors`,
+ * host struct `hp`). `workspace` is a device buffer of at least
+ * ma_muon_workspace_bytes() bytes, 256-byte aligned, owned by the caller and
+ * free for the library's use until the enqueued work completes; its contents
+ * on entry do not matter. Enqueues: the fused momentum/Nesterov/norm pass,
+ * ns_steps x (Gram, A^2 -> bA + cA^2, aX + BX) batched over all matrices,
+ * the optional NorMuon / Muon+ reductions, and the fused scale/decay/apply.
+ */
+ma_status muon_step(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * One tensor stepped by AdamW (dew.training.optim: optax.adamw; speedtronic
+ * "v2 optimizers": torch AdamW). param (param_dtype), grad (grad_dtype), m and
+ * v (fp32) are device arrays of `numel` elements; param, m, v are updated in
+ * place. grad == NULL skips the tensor.
+ */
+typedef struct {
+  void* param;
+  const void* grad;
+  float* m;
+  float* v;
+  int64_t numel;
+  int32_t param_dtype;
+  int32_t grad_dtype;
+  float lr;
+  float weight_decay;
+} ma_adamw_tensor;
+
+/*
+ * m <- beta1 m + (1-beta1) g; v <- beta2 v + (1-beta2) g^2;
+ * p <- p - lr * ( (m/(1-beta1^step)) / (sqrt(v/(1-beta2^step)) + eps) + wd p ).
+ * step >= 1 counts successful updates (the caller's host counter).
+ */
+typedef struct {
+  float beta1;
+  float beta2;
+  float eps;
+  int32_t pad_;
+  int64_t step;
+} ma_adamw_hparams;
+
+/* The AdamW half of the hybrid step over `n` tensors; no workspace. */
+ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_hparams* hp,
+                     void* stream);
+
+/* Thread-local message for the last non-OK status of this thread. */
+const char* ma_last_error(void);
+
+/*
+ * Newton-Schulz alone (speedtronic "Newton-Schulz": newton_schulz(matrix,
+ * steps, eps)) on `batch` stored rows x cols matrices of `dtype` at device
+ * `in`, written to device `out` (same shape and dtype; may equal `in`). Uses
+ * hp's ns_* fields only. Workspace as for muon_step, sized by
+ * ma_newton_schulz_workspace_bytes().
+ */
+size_t ma_newton_schulz_workspace_bytes(int64_t batch, int64_t rows, int64_t cols,
+                                        int32_t dtype, const ma_muon_hparams* hp);
+ma_status ma_newton_schulz(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols,
+                           int32_t dtype, const ma_muon_hparams* hp, void* workspace,
+                           size_t workspace_bytes, void* stream);
+
+/*
+ * Host-only description of how muon_step lays out matrix `k` (0-based, in
+ * tensor order, then batch entry, then view) of a tensor list. Tensors with a
+ * NULL grad contribute no matrices. Used by tests and by callers that read the
+ * orthogonalised update from the workspace after a step.
+ */
+typedef struct {
+  int32_t tensor;        /* index into the tensor list                        */
+  int32_t batch_index;
+  int32_t view;
+  int32_t m, n;          /* stored shape of the view                          */
+  int32_t r, c;          /* canonical shape: min, max                         */
+  int32_t rp, cp;        /* canonical shape padded to the GEMM tile           */
+  int32_t transposed;    /* 1 iff m > n                                       */
+  int32_t bucket;        /* index of its (r, c) shape bucket                  */
+  float scale;           /* sqrt(max(1, m/n))                                 */
+  int32_t pad_;
+  uint64_t u_offset;     /* workspace byte offset of the final Newton-Schulz
+                            output: rp x cp row-major, ns dtype, canonical
+                            orientation, zero outside r x c                   */
+} ma_matrix_info;
+
+/* Number of matrices and shape buckets muon_step would form (host only). */
+ma_status ma_muon_plan_counts(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
+                              int32_t* n_matrices, int32_t* n_buckets);
+ma_status ma_muon_matrix_info(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
+                              int32_t k, ma_matrix_info* info);
+
+/*
+ * Per-kernel timing with HIP events, a profiling aid (not needed for use).
+ * Between ma_profile_begin() and ma_profile_end() on one host thread, every
+ * kernel that muon_step, ma_newton_schulz or adamw_step enqueues is bracketed
+ * by two events recorded on the same stream. ma_profile_end() waits for those
+ * events, writes at most `max` entries (host array `out`, one per kernel name,
+ * in first-launch order) and returns how many it wrote, or -1 on a HIP error.
+ * Recording adds an event pair per launch, so time whole steps separately.
+ */
+typedef struct {
+  char name[48];
+  int64_t launches;
+  double total_ms;
+} ma_kernel_time;
+
+ma_status ma_profile_begin(void);
+int32_t ma_profile_end(ma_kernel_time* out, int32_t max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MUON_ADAMW_H */

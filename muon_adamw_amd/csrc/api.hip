@@ -1,0 +1,705 @@
+// C ABI of the hybrid Muon + AdamW step: argument validation, the
+// shape-bucketing planner, the launch-table upload and the launch sequence.
+//
+// Planner: every Muon tensor is expanded into its matrices (batch entries x
+// row views; kimi-k3 "Optimization", matrix views; dew.training.optim,
+// BATCH_AXES), each matrix is put in canonical orientation (r = min(m, n)
+// rows; speedtronic "Newton-Schulz": tall matrices are transposed), padded to
+// the GEMM tile, grouped into (r, c) shape buckets, and given its workspace
+// buffers. Each kernel launch then covers every matrix at once through a tile
+// map whose order puts the buckets with the longest tiles first, so one launch
+// per Newton-Schulz product serves the whole step.
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cmath>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "muon_adamw.h"
+#include "kernels.hpp"
+
+using namespace ma;
+
+namespace {
+
+thread_local std::string g_err;
+
+ma_status fail(ma_status s, const std::string& msg) {
+  g_err = msg;
+  return s;
+}
+
+constexpr size_t kAlign = 256;
+size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
+int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
+size_t dtype_size(int32_t dt) { return dt == MA_BF16 ? 2 : 4; }
+bool dtype_ok(int32_t dt) { return dt == MA_F32 || dt == MA_BF16; }
+
+// ---------------------------------------------------------------------------
+// Plan
+// ---------------------------------------------------------------------------
+struct MatPlan {
+  int tensor, bidx, view;
+  int m, n, r, c, rp, cp, tall, bucket;
+  float scale;
+  int64_t elem_off;   // element offset of the view inside its tensor
+  int64_t rowv_off;   // offset of the view's first row in row_v
+  int ntile_ew;
+  size_t off_x0, off_x1, off_a, off_b, off_part, off_stat, off_csr, off_csc, off_rf, off_cf;
+};
+
+struct MapRef {
+  size_t start_off = 0, perm_off = 0;  // byte offsets inside the table region
+  int nmat = 0, total = 0;
+};
+
+struct Plan {
+  std::vector<MatPlan> mats;
+  int nbuckets = 0;
+  int ns_dt = MA_BF16;
+  int gemm_tile = 128;
+  std::vector<int32_t> ints;
+  size_t desc_bytes = 0, table_bytes = 0, ws_bytes = 0;
+  MapRef ew, perm1, sym, app, rows_nt, cols_t, rows_t, cols_nt, fin_all, out;
+};
+
+struct Item {
+  int mat;
+  int tiles;
+  int64_t key;  // larger first
+};
+
+MapRef add_map(Plan& P, std::vector<Item> items) {
+  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.key > y.key; });
+  MapRef r;
+  r.nmat = static_cast<int>(items.size());
+  r.start_off = P.ints.size() * sizeof(int32_t);
+  int64_t acc = 0;
+  for (const Item& it : items) {
+    P.ints.push_back(static_cast<int32_t>(acc));
+    acc += it.tiles;
+  }
+  P.ints.push_back(static_cast<int32_t>(acc));
+  r.perm_off = P.ints.size() * sizeof(int32_t);
+  for (const Item& it : items) P.ints.push_back(it.mat);
+  r.total = static_cast<int>(acc);
+  return r;
+}
+
+ma_status validate_hparams(const ma_muon_hparams* hp) {
+  if (!hp) return fail(MA_E_INVALID, "hparams is NULL");
+  if (!(hp->beta >= 0.f && hp->beta < 1.f)) return fail(MA_E_INVALID, "beta must be in [0, 1)");
+  if (hp->nesterov != 0 && hp->nesterov != 1) return fail(MA_E_INVALID, "nesterov must be 0 or 1");
+  if (hp->ns_steps < 1 || hp->ns_steps > 64) return fail(MA_E_INVALID, "ns_steps must be in [1, 64]");
+  if (!std::isfinite(hp->ns_a) || !std::isfinite(hp->ns_b) || !std::isfinite(hp->ns_c))
+    return fail(MA_E_INVALID, "Newton-Schulz coefficients must be finite");
+  if (!(hp->ns_eps >= 0.f) || !std::isfinite(hp->ns_eps)) return fail(MA_E_INVALID, "ns_eps must be finite and >= 0");
+  if (!dtype_ok(hp->ns_dtype)) return fail(MA_E_DTYPE, "ns_dtype must be MA_F32 or MA_BF16");
+  if (hp->normuon != 0 && hp->normuon != 1) return fail(MA_E_INVALID, "normuon must be 0 or 1");
+  if (hp->muon_plus != 0 && hp->muon_plus != 1) return fail(MA_E_INVALID, "muon_plus must be 0 or 1");
+  if (hp->normuon && hp->muon_plus)
+    return fail(MA_E_UNSUPPORTED, "NorMuon and Muon+ together are not defined; enable one");
+  if (hp->normuon && !(hp->normuon_beta2 >= 0.f && hp->normuon_beta2 <= 1.f))
+    return fail(MA_E_INVALID, "normuon_beta2 must be in [0, 1]");
+  if (hp->muon_plus && !(hp->muon_plus_eps >= 0.f && std::isfinite(hp->muon_plus_eps)))
+    return fail(MA_E_INVALID, "muon_plus_eps must be finite and >= 0");
+  if (hp->cautious < MA_CAUTIOUS_NONE || hp->cautious > MA_CAUTIOUS_WRAPPER)
+    return fail(MA_E_INVALID, "cautious must be 0 (none), 1 (weight-decay mask) or 2 (wrapper)");
+  return MA_OK;
+}
+
+struct Range {
+  uintptr_t lo, hi;
+  int tensor;
+  const char* what;
+};
+
+ma_status check_overlaps(std::vector<Range>& rs) {
+  std::sort(rs.begin(), rs.end(), [](const Range& a, const Range& b) { return a.lo < b.lo; });
+  for (size_t i = 1; i < rs.size(); ++i) {
+    if (rs[i].lo < rs[i - 1].hi)
+      return fail(MA_E_ALIAS, std::string("overlapping buffers: ") + rs[i - 1].what + " of tensor " +
+                                  std::to_string(rs[i - 1].tensor) + " and " + rs[i].what + " of tensor " +
+                                  std::to_string(rs[i].tensor) + " (tied weights must be passed once)");
+  }
+  return MA_OK;
+}
+
+// Validates the list and builds the plan. `ns_only`: the Newton-Schulz-only
+// entry (no momentum, param = output).
+ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* hp, bool ns_only, Plan& P) {
+  ma_status st = validate_hparams(hp);
+  if (st != MA_OK) return st;
+  if (n < 0) return fail(MA_E_INVALID, "tensor count is negative");
+  if (n > 0 && !t) return fail(MA_E_INVALID, "tensor array is NULL");
+  P = Plan();
+  P.ns_dt = hp->ns_dtype;
+  P.gemm_tile = hp->ns_dtype == MA_BF16 ? 128 : 64;
+  std::vector<Range> ranges;
+  for (int i = 0; i < n; ++i) {
+    const ma_muon_tensor& x = t[i];
+    const std::string who = "tensor " + std::to_string(i) + ": ";
+    if (!dtype_ok(x.param_dtype) || !dtype_ok(x.grad_dtype))
+      return fail(MA_E_DTYPE, who + "param/grad dtype must be MA_F32 or MA_BF16 (complex is not supported)");
+    if (!x.param) return fail(MA_E_INVALID, who + "param is NULL");
+    if (x.batch < 1 || x.rows < 1 || x.cols < 1) return fail(MA_E_INVALID, who + "batch, rows and cols must be >= 1");
+    if (x.views < 1 || x.rows % x.views != 0) return fail(MA_E_INVALID, who + "views must be >= 1 and divide rows");
+    if (x.rows / x.views > 65536 || x.cols > 65536)
+      return fail(MA_E_UNSUPPORTED, who + "matrix dimensions above 65536 are not supported");
+    if (x.batch * x.views > (1 << 20)) return fail(MA_E_UNSUPPORTED, who + "too many matrices");
+    if (!std::isfinite(x.lr) || !std::isfinite(x.weight_decay))
+      return fail(MA_E_INVALID, who + "lr and weight_decay must be finite");
+    if (!x.grad) continue;
+    if (!ns_only && !x.momentum) return fail(MA_E_INVALID, who + "momentum is NULL");
+    if (hp->normuon && !x.row_v) return fail(MA_E_INVALID, who + "NorMuon needs row_v");
+    const uintptr_t numel = static_cast<uintptr_t>(x.batch * x.rows * x.cols);
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(x.param);
+    if (pb % dtype_size(x.param_dtype) || reinterpret_cast<uintptr_t>(x.grad) % dtype_size(x.grad_dtype))
+      return fail(MA_E_INVALID, who + "param/grad not aligned to their element size");
+    ranges.push_back({pb, pb + numel * dtype_size(x.param_dtype), i, "param"});
+    if (!ns_only) {
+      const uintptr_t mb = reinterpret_cast<uintptr_t>(x.momentum);
+      if (mb % 4) return fail(MA_E_INVALID, who + "momentum not 4-byte aligned");
+      ranges.push_back({mb, mb + numel * 4, i, "momentum"});
+    }
+    if (hp->normuon) {
+      const uintptr_t vb = reinterpret_cast<uintptr_t>(x.row_v);
+      if (vb % 4) return fail(MA_E_INVALID, who + "row_v not 4-byte aligned");
+      ranges.push_back({vb, vb + static_cast<uintptr_t>(x.batch * x.rows) * 4, i, "row_v"});
+    }
+  }
+  if (!ns_only) {
+    st = check_overlaps(ranges);
+    if (st != MA_OK) return st;
+  }
+
+  // Expand into matrices, canonicalise, bucket.
+  std::map<std::pair<int, int>, int> buckets;
+  for (int i = 0; i < n; ++i) {
+    const ma_muon_tensor& x = t[i];
+    if (!x.grad) continue;
+    const int m = static_cast<int>(x.rows / x.views), nn = static_cast<int>(x.cols);
+    for (int64_t b = 0; b < x.batch; ++b)
+      for (int v = 0; v < x.views; ++v) {
+        MatPlan mp{};
+        mp.tensor = i;
+        mp.bidx = static_cast<int>(b);
+        mp.view = v;
+        mp.m = m;
+        mp.n = nn;
+        mp.tall = m > nn;
+        mp.r = std::min(m, nn);
+        mp.c = std::max(m, nn);
+        mp.rp = static_cast<int>(round_up(mp.r, kPad));
+        mp.cp = static_cast<int>(round_up(mp.c, kPad));
+        mp.scale = static_cast<float>(std::sqrt(std::max(1.0, static_cast<double>(m) / nn)));
+        mp.elem_off = b * x.rows * x.cols + static_cast<int64_t>(v) * m * x.cols;
+        mp.rowv_off = b * x.rows + static_cast<int64_t>(v) * m;
+        mp.ntile_ew = (mp.rp / kEw) * (mp.cp / kEw);
+        auto key = std::make_pair(mp.r, mp.c);
+        auto it = buckets.find(key);
+        if (it == buckets.end()) it = buckets.emplace(key, static_cast<int>(buckets.size())).first;
+        mp.bucket = it->second;
+        if (static_cast<int64_t>(mp.rp) * mp.cp > (int64_t(1) << 31) - 1)
+          return fail(MA_E_UNSUPPORTED, "tensor " + std::to_string(i) + ": matrix too large");
+        P.mats.push_back(mp);
+      }
+  }
+  P.nbuckets = static_cast<int>(buckets.size());
+  const int nm = static_cast<int>(P.mats.size());
+  if (nm > (1 << 22)) return fail(MA_E_UNSUPPORTED, "too many matrices in one call");
+
+  // Tile maps.
+  const int T = P.gemm_tile;
+  std::vector<Item> ew, fin, sym, app, rows_nt, cols_t, rows_t, cols_nt, out;
+  int64_t tot_ew = 0, tot_sym = 0, tot_app = 0, tot_out = 0;
+  for (int k = 0; k < nm; ++k) {
+    const MatPlan& mp = P.mats[k];
+    const int nt = mp.rp / T;
+    ew.push_back({k, mp.ntile_ew, 0});
+    fin.push_back({k, 1, 0});
+    sym.push_back({k, nt * (nt + 1) / 2, static_cast<int64_t>(mp.cp) * 4 + mp.rp});  // Gram tile work ~ cp
+    app.push_back({k, nt * (mp.cp / T), mp.rp});
+    const int rows_blocks = (mp.r + 3) / 4, col_blocks = (mp.c + 63) / 64;
+    if (mp.tall) { cols_t.push_back({k, col_blocks, 0}); rows_t.push_back({k, rows_blocks, 0}); }
+    else { rows_nt.push_back({k, rows_blocks, 0}); cols_nt.push_back({k, col_blocks, 0}); }
+    out.push_back({k, ((mp.m + kEw - 1) / kEw) * ((mp.n + kEw - 1) / kEw), 0});
+    tot_ew += mp.ntile_ew;
+    tot_sym += nt * (nt + 1) / 2;
+    tot_app += static_cast<int64_t>(nt) * (mp.cp / T);
+    tot_out += static_cast<int64_t>((mp.m + kEw - 1) / kEw) * ((mp.n + kEw - 1) / kEw);
+  }
+  const int64_t kMaxGrid = (int64_t(1) << 31) - 1;
+  if (tot_ew > kMaxGrid || tot_sym > kMaxGrid || tot_app > kMaxGrid || tot_out > kMaxGrid)
+    return fail(MA_E_UNSUPPORTED, "step too large for one launch");
+  P.ew = add_map(P, ew);
+  P.fin_all = add_map(P, fin);
+  P.sym = add_map(P, sym);
+  P.app = add_map(P, app);
+  P.rows_nt = add_map(P, rows_nt);
+  P.cols_t = add_map(P, cols_t);
+  P.rows_t = add_map(P, rows_t);
+  P.cols_nt = add_map(P, cols_nt);
+  P.out = add_map(P, out);
+
+  // Workspace layout: [MatDesc x nm][int tables] then per-matrix buffers.
+  P.desc_bytes = align_up(sizeof(MatDesc) * std::max(nm, 1));
+  P.table_bytes = P.desc_bytes + align_up(P.ints.size() * sizeof(int32_t));
+  size_t off = P.table_bytes;
+  const size_t es = dtype_size(hp->ns_dtype);
+  for (MatPlan& mp : P.mats) {
+    const size_t xb = align_up(static_cast<size_t>(mp.rp) * mp.cp * es);
+    const size_t ab = align_up(static_cast<size_t>(mp.rp) * mp.rp * es);
+    mp.off_x0 = off; off += xb;
+    mp.off_x1 = off; off += xb;
+    mp.off_a = off; off += ab;
+    mp.off_b = off; off += ab;
+    mp.off_part = off; off += align_up(static_cast<size_t>(mp.ntile_ew) * 4);
+    mp.off_stat = off; off += kAlign;
+    mp.off_csr = off; off += align_up(static_cast<size_t>(mp.rp) * 4);
+    mp.off_csc = off; off += align_up(static_cast<size_t>(mp.cp) * 4);
+    mp.off_rf = off; off += align_up(static_cast<size_t>(mp.m) * 4);
+    mp.off_cf = off; off += align_up(static_cast<size_t>(mp.n) * 4);
+  }
+  P.ws_bytes = off;
+  return MA_OK;
+}
+
+TileMap device_map(const MapRef& r, char* tables, size_t desc_bytes) {
+  TileMap tm;
+  tm.start = reinterpret_cast<const int32_t*>(tables + desc_bytes + r.start_off);
+  tm.perm = reinterpret_cast<const int32_t*>(tables + desc_bytes + r.perm_off);
+  tm.nmat = r.nmat;
+  tm.total = r.total;
+  return tm;
+}
+
+// Pinned staging ring for the launch tables: a slot is reused only after the
+// copy it last fed has completed (an event from four calls earlier).
+struct Staging {
+  void* host = nullptr;
+  size_t cap = 0;
+  hipEvent_t ev = nullptr;
+  bool used = false;
+};
+struct DevState {
+  Staging ring[4];
+  unsigned next = 0;
+};
+std::mutex g_mu;
+std::map<int, DevState> g_dev;
+
+ma_status upload(const std::vector<char>& host, void* dst, hipStream_t s) {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return fail(MA_E_HIP, "hipGetDevice failed");
+  std::lock_guard<std::mutex> lk(g_mu);
+  DevState& ds = g_dev[dev];
+  Staging& st = ds.ring[ds.next++ % 4];
+  if (st.used && hipEventSynchronize(st.ev) != hipSuccess) return fail(MA_E_HIP, "staging event wait failed");
+  if (st.cap < host.size()) {
+    if (st.host) (void)hipHostFree(st.host);
+    st.host = nullptr;
+    st.cap = 0;
+    if (hipHostMalloc(&st.host, host.size(), hipHostMallocDefault) != hipSuccess)
+      return fail(MA_E_HIP, "pinned staging allocation failed");
+    st.cap = host.size();
+  }
+  if (!st.ev && hipEventCreateWithFlags(&st.ev, hipEventDisableTiming) != hipSuccess)
+    return fail(MA_E_HIP, "event creation failed");
+  std::memcpy(st.host, host.data(), host.size());
+  if (hipMemcpyAsync(dst, st.host, host.size(), hipMemcpyHostToDevice, s) != hipSuccess)
+    return fail(MA_E_HIP, "table upload failed");
+  if (hipEventRecord(st.ev, s) != hipSuccess) return fail(MA_E_HIP, "event record failed");
+  st.used = true;
+  return MA_OK;
+}
+
+// ---------------------------------------------------------------------------
+// Optional per-kernel event timing (ma_profile_begin / ma_profile_end)
+// ---------------------------------------------------------------------------
+struct ProfRec {
+  const char* name;
+  hipEvent_t e0, e1;
+};
+struct ProfState {
+  bool on = false;
+  std::vector<ProfRec> recs;
+  std::vector<hipEvent_t> pool;
+};
+thread_local ProfState g_prof;
+
+hipEvent_t prof_event() {
+  if (!g_prof.pool.empty()) {
+    hipEvent_t e = g_prof.pool.back();
+    g_prof.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Runs `launch`; when profiling, brackets it with events on `s`.
+template <typename F>
+void timed(const char* name, hipStream_t s, F&& launch) {
+  if (!g_prof.on) {
+    launch();
+    return;
+  }
+  ProfRec r{name, prof_event(), prof_event()};
+  if (r.e0) (void)hipEventRecord(r.e0, s);
+  launch();
+  if (r.e1) (void)hipEventRecord(r.e1, s);
+  if (r.e0 && r.e1) g_prof.recs.push_back(r);
+}
+
+// Fills the descriptors for a workspace at `ws` and enqueues the whole step.
+ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams* hp, bool ns_only, void* ws,
+                   hipStream_t s) {
+  const int nm = static_cast<int>(P.mats.size());
+  if (nm == 0) return MA_OK;
+  char* base = static_cast<char*>(ws);
+  std::vector<char> host(P.table_bytes, 0);
+  MatDesc* D = reinterpret_cast<MatDesc*>(host.data());
+  for (int k = 0; k < nm; ++k) {
+    const MatPlan& mp = P.mats[k];
+    const ma_muon_tensor& x = t[mp.tensor];
+    const size_t pes = dtype_size(x.param_dtype), ges = dtype_size(x.grad_dtype);
+    MatDesc& d = D[k];
+    d.param = static_cast<char*>(x.param) + mp.elem_off * pes;
+    d.grad = static_cast<const char*>(x.grad) + mp.elem_off * ges;
+    d.mom = ns_only ? nullptr : x.momentum + mp.elem_off;
+    d.row_v = (hp->normuon && x.row_v) ? x.row_v + mp.rowv_off : nullptr;
+    d.m = mp.m; d.n = mp.n; d.r = mp.r; d.c = mp.c; d.rp = mp.rp; d.cp = mp.cp;
+    d.tall = mp.tall;
+    d.pdt = x.param_dtype;
+    d.gdt = x.grad_dtype;
+    const uintptr_t al = reinterpret_cast<uintptr_t>(d.param) | reinterpret_cast<uintptr_t>(d.grad) |
+                         reinterpret_cast<uintptr_t>(d.mom);
+    d.vec = (mp.n % 4 == 0) && (al % 16 == 0);
+    const double lr = x.lr, wd = x.weight_decay;
+    d.decay = static_cast<float>(1.0 - lr * wd);
+    d.lrwd = static_cast<float>(lr * wd);
+    d.step = static_cast<float>(lr * mp.scale);
+    d.scale = mp.scale;
+    d.x0 = base + mp.off_x0;
+    d.x1 = base + mp.off_x1;
+    d.a = base + mp.off_a;
+    d.b = base + mp.off_b;
+    d.part = reinterpret_cast<float*>(base + mp.off_part);
+    d.stat = reinterpret_cast<float*>(base + mp.off_stat);
+    d.csum_r = reinterpret_cast<float*>(base + mp.off_csr);
+    d.csum_c = reinterpret_cast<float*>(base + mp.off_csc);
+    d.rfac = reinterpret_cast<float*>(base + mp.off_rf);
+    d.cfac = reinterpret_cast<float*>(base + mp.off_cf);
+    d.ntile_ew = mp.ntile_ew;
+  }
+  std::memcpy(host.data() + P.desc_bytes, P.ints.data(), P.ints.size() * sizeof(int32_t));
+  ma_status st = upload(host, ws, s);
+  if (st != MA_OK) return st;
+
+  const MatDesc* mats = reinterpret_cast<const MatDesc*>(base);
+  auto TM = [&](const MapRef& r) { return device_map(r, base, P.desc_bytes); };
+  const float beta = hp->beta;
+  const float omb = static_cast<float>(1.0 - static_cast<double>(hp->beta));
+  (void)hipGetLastError();
+  const int ew_dt = P.ns_dt;
+  timed("momentum", s, [&] { launch_momentum(mats, TM(P.ew), ew_dt, beta, omb, hp->nesterov, s); });
+  timed("norm_finalize", s, [&] { launch_norm_finalize(mats, TM(P.fin_all), hp->ns_eps, s); });
+  static const char* const kNsNames[2][3] = {{"ns_gram_f32", "ns_square_f32", "ns_apply_f32"},
+                                             {"ns_gram_bf16", "ns_square_bf16", "ns_apply_bf16"}};
+  const int bf = P.ns_dt == MA_BF16;
+  for (int it = 0; it < hp->ns_steps; ++it) {
+    for (int op = NS_GRAM; op <= NS_APPLY; ++op) {
+      const TileMap tm = TM(op == NS_APPLY ? P.app : P.sym);
+      timed(kNsNames[bf][op], s, [&] {
+        if (bf)
+          launch_ns_bf16(op, mats, tm, it & 1, it == 0, hp->ns_a, hp->ns_b, hp->ns_c, s);
+        else
+          launch_ns_f32(op, mats, tm, it & 1, it == 0, hp->ns_a, hp->ns_b, hp->ns_c, s);
+      });
+    }
+  }
+  const int src = hp->ns_steps & 1;  // buffer holding the final output
+  int use_rf = 0, use_cf = 0;
+  if (!ns_only && (hp->normuon || hp->muon_plus)) {
+    if (P.rows_nt.nmat) timed("rowsum", s, [&] { launch_canon_rowsum(mats, TM(P.rows_nt), P.ns_dt, src, 0, s); });
+    if (P.cols_t.nmat) timed("colsum", s, [&] { launch_canon_colsum(mats, TM(P.cols_t), P.ns_dt, src, 0, s); });
+  }
+  if (!ns_only && hp->normuon) {
+    timed("finalize_normuon", s, [&] { launch_finalize_normuon(mats, TM(P.fin_all), hp->normuon_beta2, s); });
+    use_rf = 1;
+  }
+  if (!ns_only && hp->muon_plus) {
+    timed("finalize_muon_plus", s,
+          [&] { launch_finalize_muon_plus(mats, TM(P.fin_all), 1, hp->muon_plus_eps, s); });
+    if (P.cols_nt.nmat) timed("colsum", s, [&] { launch_canon_colsum(mats, TM(P.cols_nt), P.ns_dt, src, 1, s); });
+    if (P.rows_t.nmat) timed("rowsum", s, [&] { launch_canon_rowsum(mats, TM(P.rows_t), P.ns_dt, src, 1, s); });
+    timed("finalize_muon_plus", s,
+          [&] { launch_finalize_muon_plus(mats, TM(P.fin_all), 2, hp->muon_plus_eps, s); });
+    use_rf = use_cf = 1;
+  }
+  timed(ns_only ? "copy_out" : "apply_update", s, [&] {
+    launch_apply(mats, TM(P.out), P.ns_dt, src, ns_only ? APPLY_COPY : APPLY_UPDATE, ns_only ? 0 : hp->cautious,
+                 use_rf, use_cf, s);
+  });
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MA_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return MA_OK;
+}
+
+ma_status check_workspace(const Plan& P, void* ws, size_t bytes) {
+  if (P.mats.empty()) return MA_OK;
+  if (!ws) return fail(MA_E_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(MA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (bytes < P.ws_bytes)
+    return fail(MA_E_WORKSPACE, "workspace too small: " + std::to_string(bytes) + " < " + std::to_string(P.ws_bytes));
+  return MA_OK;
+}
+
+ma_muon_tensor ns_tensor(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols, int32_t dtype) {
+  ma_muon_tensor x{};
+  x.param = out;
+  x.grad = in;
+  x.batch = batch;
+  x.rows = rows;
+  x.cols = cols;
+  x.views = 1;
+  x.param_dtype = dtype;
+  x.grad_dtype = dtype;
+  return x;
+}
+
+ma_muon_hparams ns_hparams(const ma_muon_hparams* hp) {
+  ma_muon_hparams h = *hp;
+  h.normuon = 0;
+  h.muon_plus = 0;
+  h.cautious = 0;
+  return h;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* ma_last_error(void) { return g_err.c_str(); }
+
+size_t ma_muon_workspace_bytes(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp) {
+  Plan P;
+  if (build_plan(tensors, n, hp, false, P) != MA_OK) return 0;
+  return P.mats.empty() ? 0 : P.ws_bytes;
+}
+
+ma_status muon_step(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  Plan P;
+  ma_status st = build_plan(tensors, n, hp, false, P);
+  if (st != MA_OK) return st;
+  st = check_workspace(P, workspace, workspace_bytes);
+  if (st != MA_OK) return st;
+  return run_plan(P, tensors, hp, false, workspace, static_cast<hipStream_t>(stream));
+}
+
+size_t ma_newton_schulz_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
+                                        const ma_muon_hparams* hp) {
+  if (!hp) {
+    g_err = "hparams is NULL";
+    return 0;
+  }
+  alignas(16) static const char dummy[16] = {0};
+  ma_muon_tensor x = ns_tensor(dummy, const_cast<char*>(dummy), batch, rows, cols, dtype);
+  ma_muon_hparams h = ns_hparams(hp);
+  Plan P;
+  if (build_plan(&x, 1, &h, true, P) != MA_OK) return 0;
+  return P.ws_bytes;
+}
+
+ma_status ma_newton_schulz(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
+                           const ma_muon_hparams* hp, void* workspace, size_t workspace_bytes, void* stream) {
+  if (!hp) return fail(MA_E_INVALID, "hparams is NULL");
+  if (!in || !out) return fail(MA_E_INVALID, "in/out is NULL");
+  ma_muon_tensor x = ns_tensor(in, out, batch, rows, cols, dtype);
+  ma_muon_hparams h = ns_hparams(hp);
+  Plan P;
+  ma_status st = build_plan(&x, 1, &h, true, P);
+  if (st != MA_OK) return st;
+  st = check_workspace(P, workspace, workspace_bytes);
+  if (st != MA_OK) return st;
+  return run_plan(P, &x, &h, true, workspace, static_cast<hipStream_t>(stream));
+}
+
+ma_status ma_muon_plan_counts(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
+                              int32_t* n_matrices, int32_t* n_buckets) {
+  Plan P;
+  ma_status st = build_plan(tensors, n, hp, false, P);
+  if (st != MA_OK) return st;
+  if (n_matrices) *n_matrices = static_cast<int32_t>(P.mats.size());
+  if (n_buckets) *n_buckets = P.nbuckets;
+  return MA_OK;
+}
+
+ma_status ma_muon_matrix_info(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp, int32_t k,
+                              ma_matrix_info* info) {
+  if (!info) return fail(MA_E_INVALID, "info is NULL");
+  Plan P;
+  ma_status st = build_plan(tensors, n, hp, false, P);
+  if (st != MA_OK) return st;
+  if (k < 0 || k >= static_cast<int32_t>(P.mats.size())) return fail(MA_E_INVALID, "matrix index out of range");
+  const MatPlan& mp = P.mats[k];
+  std::memset(info, 0, sizeof(*info));
+  info->tensor = mp.tensor;
+  info->batch_index = mp.bidx;
+  info->view = mp.view;
+  info->m = mp.m;
+  info->n = mp.n;
+  info->r = mp.r;
+  info->c = mp.c;
+  info->rp = mp.rp;
+  info->cp = mp.cp;
+  info->transposed = mp.tall;
+  info->bucket = mp.bucket;
+  info->scale = mp.scale;
+  info->u_offset = (hp->ns_steps & 1) ? mp.off_x1 : mp.off_x0;
+  return MA_OK;
+}
+
+ma_status ma_profile_begin(void) {
+  for (ProfRec& r : g_prof.recs) {
+    g_prof.pool.push_back(r.e0);
+    g_prof.pool.push_back(r.e1);
+  }
+  g_prof.recs.clear();
+  g_prof.on = true;
+  return MA_OK;
+}
+
+int32_t ma_profile_end(ma_kernel_time* out, int32_t max) {
+  g_prof.on = false;
+  std::vector<std::string> names;
+  std::vector<int64_t> counts;
+  std::vector<double> totals;
+  int32_t rc = 0;
+  for (ProfRec& r : g_prof.recs) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.e1) != hipSuccess || hipEventElapsedTime(&ms, r.e0, r.e1) != hipSuccess) {
+      g_err = "profiling event query failed";
+      rc = -1;
+      break;
+    }
+    size_t k = 0;
+    while (k < names.size() && names[k] != r.name) ++k;
+    if (k == names.size()) {
+      names.push_back(r.name);
+      counts.push_back(0);
+      totals.push_back(0.0);
+    }
+    counts[k] += 1;
+    totals[k] += ms;
+  }
+  for (ProfRec& r : g_prof.recs) {
+    g_prof.pool.push_back(r.e0);
+    g_prof.pool.push_back(r.e1);
+  }
+  g_prof.recs.clear();
+  if (rc < 0) return rc;
+  int32_t w = 0;
+  for (size_t k = 0; k < names.size() && w < max && out; ++k, ++w) {
+    std::memset(&out[w], 0, sizeof(out[w]));
+    std::strncpy(out[w].name, names[k].c_str(), sizeof(out[w].name) - 1);
+    out[w].launches = counts[k];
+    out[w].total_ms = totals[k];
+  }
+  return w;
+}
+
+ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_hparams* hp, void* stream) {
+  if (!hp) return fail(MA_E_INVALID, "hparams is NULL");
+  if (n < 0) return fail(MA_E_INVALID, "tensor count is negative");
+  if (n > 0 && !tensors) return fail(MA_E_INVALID, "tensor array is NULL");
+  if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f))
+    return fail(MA_E_INVALID, "betas must be in [0, 1)");
+  if (!(hp->eps >= 0.f) || !std::isfinite(hp->eps)) return fail(MA_E_INVALID, "eps must be finite and >= 0");
+  if (hp->step < 1) return fail(MA_E_INVALID, "step must be >= 1");
+  std::vector<Range> ranges;
+  for (int i = 0; i < n; ++i) {
+    const ma_adamw_tensor& x = tensors[i];
+    const std::string who = "tensor " + std::to_string(i) + ": ";
+    if (!dtype_ok(x.param_dtype) || !dtype_ok(x.grad_dtype))
+      return fail(MA_E_DTYPE, who + "param/grad dtype must be MA_F32 or MA_BF16 (complex is not supported)");
+    if (x.numel < 0) return fail(MA_E_INVALID, who + "numel is negative");
+    if (!std::isfinite(x.lr) || !std::isfinite(x.weight_decay))
+      return fail(MA_E_INVALID, who + "lr and weight_decay must be finite");
+    if (!x.grad || x.numel == 0) continue;
+    if (!x.param || !x.m || !x.v) return fail(MA_E_INVALID, who + "param, m and v must not be NULL");
+    if (x.numel > (int64_t(1) << 40)) return fail(MA_E_UNSUPPORTED, who + "tensor too large");
+    const uintptr_t pb = reinterpret_cast<uintptr_t>(x.param), mb = reinterpret_cast<uintptr_t>(x.m),
+                    vb = reinterpret_cast<uintptr_t>(x.v);
+    if (pb % dtype_size(x.param_dtype) || mb % 4 || vb % 4 ||
+        reinterpret_cast<uintptr_t>(x.grad) % dtype_size(x.grad_dtype))
+      return fail(MA_E_INVALID, who + "buffers not aligned to their element size");
+    const uintptr_t ne = static_cast<uintptr_t>(x.numel);
+    ranges.push_back({pb, pb + ne * dtype_size(x.param_dtype), i, "param"});
+    ranges.push_back({mb, mb + ne * 4, i, "m"});
+    ranges.push_back({vb, vb + ne * 4, i, "v"});
+  }
+  ma_status st = check_overlaps(ranges);
+  if (st != MA_OK) return st;
+  if (ranges.empty()) return MA_OK;  // nothing to step: no HIP call at all
+
+  AdamLaunch L{};
+  const double b1 = hp->beta1, b2 = hp->beta2;
+  L.b1 = hp->beta1;
+  L.omb1 = static_cast<float>(1.0 - b1);
+  L.b2 = hp->beta2;
+  L.omb2 = static_cast<float>(1.0 - b2);
+  L.eps = hp->eps;
+  L.inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(b1, static_cast<double>(hp->step))));
+  L.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(b2, static_cast<double>(hp->step))));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  int64_t blocks = 0;
+  auto flush = [&]() {
+    if (L.nt == 0) return;
+    L.block_start[L.nt] = static_cast<int32_t>(blocks);
+    timed("adamw", s, [&] { launch_adamw(L, static_cast<int>(blocks), s); });
+    L.nt = 0;
+    blocks = 0;
+  };
+  for (int i = 0; i < n; ++i) {
+    const ma_adamw_tensor& x = tensors[i];
+    if (!x.grad || x.numel == 0) continue;
+    int64_t nb = (x.numel + kAdamChunk - 1) / kAdamChunk;
+    int64_t done = 0;
+    while (nb > 0) {
+      // split very large tensors so block indices stay in int32
+      const int64_t room = (int64_t(1) << 30) - blocks;
+      const int64_t take = std::min(nb, room);
+      AdamTensorArg& a = L.t[L.nt];
+      a.p = static_cast<char*>(x.param) + done * kAdamChunk * dtype_size(x.param_dtype);
+      a.g = static_cast<const char*>(x.grad) + done * kAdamChunk * dtype_size(x.grad_dtype);
+      a.m = x.m + done * kAdamChunk;
+      a.v = x.v + done * kAdamChunk;
+      a.numel = std::min(x.numel - done * kAdamChunk, take * kAdamChunk);
+      a.pdt = x.param_dtype;
+      a.gdt = x.grad_dtype;
+      a.lr = x.lr;
+      a.wd = x.weight_decay;
+      L.block_start[L.nt] = static_cast<int32_t>(blocks);
+      blocks += take;
+      ++L.nt;
+      done += take;
+      nb -= take;
+      if (L.nt == kMaxAdamTensors || blocks >= (int64_t(1) << 30)) flush();
+    }
+  }
+  flush();
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MA_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return MA_OK;
+}
+
+}  // extern "C"

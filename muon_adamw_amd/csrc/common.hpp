@@ -1,0 +1,100 @@
+// Shared host/device definitions of the Muon + AdamW library (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace ma {
+
+enum : int32_t { DT_F32 = 0, DT_BF16 = 1 };
+enum : int32_t { CAUT_NONE = 0, CAUT_WD_MASK = 1, CAUT_WRAPPER = 2 };
+
+// Canonical buffers are padded to multiples of this many rows and columns, so
+// every Newton-Schulz GEMM tile is full. Zero padding is exact: zero rows and
+// columns stay zero through X X^T, A^2 and B X.
+constexpr int kPad = 128;
+// Element tile of the momentum pass, the reductions and the apply pass.
+constexpr int kEw = 64;
+
+// One matrix: one view of one batch entry of one Muon tensor, plus its
+// workspace buffers. Built on the host, read by every Muon kernel.
+struct MatDesc {
+  // stored view (row-major m x n, leading dimension n)
+  void* param;        // first element of the view
+  const void* grad;   // first element of the view
+  float* mom;         // first element of the view; null: Newton-Schulz only
+  float* row_v;       // NorMuon second moment of the view's m rows, or null
+  int32_t m, n;       // stored shape
+  int32_t r, c;       // canonical shape (min, max)
+  int32_t rp, cp;     // padded canonical shape
+  int32_t tall;       // m > n: canonical = stored transposed
+  int32_t pdt, gdt;   // param / grad dtype
+  int32_t vec;        // stored rows may use 16-byte accesses
+  float decay;        // 1 - lr*wd
+  float lrwd;         // lr*wd
+  float step;         // lr*scale
+  float scale;        // sqrt(max(1, m/n))
+  // workspace
+  void* x0;           // canonical rp x cp, ns dtype: Q, then X2, X4
+  void* x1;           // canonical rp x cp, ns dtype: X1, X3, X5
+  void* a;            // rp x rp Gram
+  void* b;            // rp x rp  b*A + c*A^2
+  float* part;        // sum-of-squares partial per momentum-pass tile
+  float* stat;        // [0] sigma = 1/(||Q||_F + eps)
+  float* csum_r;      // canonical row sums of squares, rp entries
+  float* csum_c;      // canonical column sums of squares, cp entries
+  float* rfac;        // per stored row factor, m entries
+  float* cfac;        // per stored column factor, n entries
+  int32_t ntile_ew;   // number of momentum-pass tiles (= partial count)
+  int32_t pad_;
+};
+
+// Maps a flat block index to (matrix, local tile) for one launch: matrices
+// are visited in `perm` order; entry k owns blocks [start[k], start[k+1]).
+struct TileMap {
+  const int32_t* start;  // nmat + 1 prefix sums
+  const int32_t* perm;   // nmat matrix indices
+  int32_t nmat;
+  int32_t total;         // start[nmat]
+};
+
+__device__ __forceinline__ int find_entry(const TileMap& tm, int blk) {
+  int lo = 0, hi = tm.nmat - 1;
+  while (lo < hi) {
+    int mid = (lo + hi + 1) >> 1;
+    if (tm.start[mid] <= blk) lo = mid; else hi = mid - 1;
+  }
+  return lo;
+}
+
+// bf16 <-> fp32. Stores round to nearest even (quiet NaN kept).
+__device__ __forceinline__ float bf16_to_f32(uint16_t h) {
+  return __uint_as_float(static_cast<uint32_t>(h) << 16);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return static_cast<uint16_t>((u >> 16) | 0x40u);
+  u += 0x7fffu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  return static_cast<uint32_t>(f32_to_bf16(lo)) | (static_cast<uint32_t>(f32_to_bf16(hi)) << 16);
+}
+
+__device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
+  return dt == DT_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i])
+                       : static_cast<const float*>(p)[i];
+}
+__device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float v) {
+  if (dt == DT_BF16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  else static_cast<float*>(p)[i] = v;
+}
+
+// Wave64 sum in a fixed butterfly order (deterministic).
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+}  // namespace ma

@@ -1,0 +1,107 @@
+// Fused scale + decoupled weight decay + apply (speedtronic "v2 optimizers"
+// page, "Muon update": W <- (1 - lr wd) W - lr max(1, rows/cols)^0.5 U), in the
+// stored orientation, with the optional per-row / per-column factors of
+// NorMuon and Muon+ and the two cautious forms:
+//   weight-decay mask (flaxchat "Optimizer" page, "Muon Algorithm" step 4):
+//     W <- W - lr s U - [U W >= 0] lr wd W
+//   wrapper (speedtronic "Cautious updates"):
+//     D = lr wd W + lr s U;  W <- (D G > 0) ? W - D : W
+// HBM-bound: reads U (canonical, transposed back through LDS for a tall
+// matrix) and W (and G for the wrapper), writes W, rounded to nearest even for
+// bf16 parameters. One 64 x 64 stored tile per block.
+#include "kernels.hpp"
+
+namespace ma {
+
+namespace {
+
+template <typename XT>
+__device__ __forceinline__ void load4(const XT* p, float* v);
+template <>
+__device__ __forceinline__ void load4<float>(const float* p, float* v) {
+  const float4 x = *reinterpret_cast<const float4*>(p);
+  v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
+}
+template <>
+__device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
+  const uint2 x = *reinterpret_cast<const uint2*>(p);
+  v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
+  v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ mats, TileMap tm, int src,
+                                                    int mode, int cautious, int use_rfac, int use_cfac) {
+  __shared__ float us[kEw][kEw + 1];
+  const int blk = blockIdx.x;
+  const int e = find_entry(tm, blk);
+  const MatDesc& d = mats[tm.perm[e]];
+  const int t = blk - tm.start[e];
+  const int m = d.m, n = d.n;
+  const int tiles_n = (n + kEw - 1) / kEw;
+  const int s0 = (t / tiles_n) * kEw, c0 = (t % tiles_n) * kEw;   // stored origin
+  const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+  const XT* U = static_cast<const XT*>(src ? d.x1 : d.x0);
+
+  // canonical tile covering this stored tile; the padded canonical buffer is
+  // at least as large as the stored extent rounded up to 64, so all reads are
+  // in bounds.
+  const int ci0 = d.tall ? c0 : s0, cj0 = d.tall ? s0 : c0;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lr = tr + 16 * p;
+    float v[4];
+    load4<XT>(U + (int64_t)(ci0 + lr) * d.cp + cj0 + tc, v);
+#pragma unroll
+    for (int u = 0; u < 4; ++u) us[lr][tc + u] = v[u];
+  }
+  __syncthreads();
+
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lr = tr + 16 * p, si = s0 + lr;
+    if (si >= m) continue;
+    const float rf = use_rfac ? d.rfac[si] : 1.f;
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sj = c0 + tc + u;
+      if (sj >= n) continue;
+      float uu = d.tall ? us[tc + u][lr] : us[lr][tc + u];
+      if (use_rfac) uu *= rf;
+      if (use_cfac) uu *= d.cfac[sj];
+      const int64_t idx = (int64_t)si * n + sj;
+      if (mode == APPLY_COPY) {
+        store_elem(d.param, idx, d.pdt, uu);
+        continue;
+      }
+      const float w = load_elem(d.param, idx, d.pdt);
+      float wn;
+      if (cautious == CAUT_NONE) {
+        wn = d.decay * w - d.step * uu;
+      } else if (cautious == CAUT_WD_MASK) {
+        wn = w - d.step * uu;
+        if (uu * w >= 0.f) wn -= d.lrwd * w;
+      } else {
+        const float g = load_elem(d.grad, idx, d.gdt);
+        const float delta = d.lrwd * w + d.step * uu;
+        wn = (delta * g > 0.f) ? w - delta : w;
+      }
+      store_elem(d.param, idx, d.pdt, wn);
+    }
+  }
+}
+
+}  // namespace
+
+void launch_apply(const MatDesc* mats, TileMap tm, int ns_dt, int src, int mode, int cautious, int use_rfac,
+                  int use_cfac, hipStream_t s) {
+  if (tm.total == 0) return;
+  if (ns_dt == DT_BF16)
+    hipLaunchKernelGGL(apply_kernel<uint16_t>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, mode, cautious,
+                       use_rfac, use_cfac);
+  else
+    hipLaunchKernelGGL(apply_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, mode, cautious,
+                       use_rfac, use_cfac);
+}
+
+}  // namespace ma

@@ -1,0 +1,154 @@
+// Fused momentum pass: B <- beta B + (1-beta) G; Q <- lerp(G, B, beta)
+// (speedtronic "v2 optimizers" page, "Muon update"; flaxchat "Optimizer" page,
+// "Muon Algorithm" step 1), written once in the canonical orientation
+// (r = min(m, n) rows) for Newton-Schulz, with the per-tile sum of squares of Q
+// for the Frobenius normalisation (speedtronic "Newton-Schulz").
+//
+// HBM-bound: reads G and B, writes B and Q (4+4+4+2 = 14 B per fp32-grad
+// element with a bf16 Q). One 64x64 canonical tile per block; a tall matrix is
+// transposed through LDS. The reduction always walks the canonical tile in the
+// same thread order, so a tall matrix and its transposed wide twin produce the
+// same bits.
+#include "kernels.hpp"
+
+namespace ma {
+
+namespace {
+
+template <typename XT>
+__device__ __forceinline__ void store4(XT* dst, const float* v);
+
+template <>
+__device__ __forceinline__ void store4<float>(float* dst, const float* v) {
+  *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+}
+template <>
+__device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, const float* v) {
+  uint2 p;
+  p.x = pack_bf16x2(v[0], v[1]);
+  p.y = pack_bf16x2(v[2], v[3]);
+  *reinterpret_cast<uint2*>(dst) = p;
+}
+
+__device__ __forceinline__ float block_sum_256(float v, float* red) {
+  v = wave_sum(v);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  if (lane == 0) red[w] = v;
+  __syncthreads();
+  float t = ((red[0] + red[1]) + red[2]) + red[3];
+  __syncthreads();
+  return t;
+}
+
+template <typename XT>
+__global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict__ mats, TileMap tm,
+                                                       float beta, float omb, int nesterov) {
+  __shared__ float qs[kEw][kEw + 1];
+  __shared__ float red[4];
+  const int blk = blockIdx.x;
+  const int e = find_entry(tm, blk);
+  const MatDesc& d = mats[tm.perm[e]];
+  const int t = blk - tm.start[e];
+  const int tiles_c = d.cp / kEw;
+  const int i0 = (t / tiles_c) * kEw, j0 = (t % tiles_c) * kEw;   // canonical origin
+  const int sr0 = d.tall ? j0 : i0, sc0 = d.tall ? i0 : j0;       // stored origin
+  const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
+  const int m = d.m, n = d.n;
+
+  // Phase 1: stored tile, coalesced along stored rows.
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int lr = tr + 16 * p, sr = sr0 + lr, sc = sc0 + tc;
+    float q[4] = {0.f, 0.f, 0.f, 0.f};
+    if (sr < m && sc < n) {
+      const int64_t idx = (int64_t)sr * n + sc;
+      float g[4];
+      if (d.vec && sc + 3 < n) {
+        if (d.gdt == DT_BF16) {
+          const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.grad) + idx);
+          g[0] = __uint_as_float(raw.x << 16); g[1] = __uint_as_float(raw.x & 0xffff0000u);
+          g[2] = __uint_as_float(raw.y << 16); g[3] = __uint_as_float(raw.y & 0xffff0000u);
+        } else {
+          const float4 raw = *reinterpret_cast<const float4*>(static_cast<const float*>(d.grad) + idx);
+          g[0] = raw.x; g[1] = raw.y; g[2] = raw.z; g[3] = raw.w;
+        }
+        if (d.mom) {
+          float4 bm = *reinterpret_cast<const float4*>(d.mom + idx);
+          float b[4] = {bm.x, bm.y, bm.z, bm.w};
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            b[u] = beta * b[u] + omb * g[u];
+            q[u] = nesterov ? g[u] + beta * (b[u] - g[u]) : b[u];
+          }
+          *reinterpret_cast<float4*>(d.mom + idx) = make_float4(b[0], b[1], b[2], b[3]);
+        } else {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) q[u] = g[u];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          if (sc + u < n) {
+            const float gu = load_elem(d.grad, idx + u, d.gdt);
+            if (d.mom) {
+              float b = d.mom[idx + u];
+              b = beta * b + omb * gu;
+              d.mom[idx + u] = b;
+              q[u] = nesterov ? gu + beta * (b - gu) : b;
+            } else {
+              q[u] = gu;
+            }
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) qs[lr][tc + u] = q[u];
+  }
+  __syncthreads();
+
+  // Phase 2: canonical tile, same thread order for both orientations.
+  XT* X = static_cast<XT*>(d.x0);
+  float ss = 0.f;
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    const int ci = tr + 16 * p;
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      v[u] = d.tall ? qs[tc + u][ci] : qs[ci][tc + u];
+      ss += v[u] * v[u];
+    }
+    store4<XT>(X + (int64_t)(i0 + ci) * d.cp + j0 + tc, v);
+  }
+  const float tot = block_sum_256(ss, red);
+  if (threadIdx.x == 0) d.part[t] = tot;
+}
+
+__global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ mats, TileMap tm,
+                                                            float eps) {
+  __shared__ float red[4];
+  const MatDesc& d = mats[tm.perm[blockIdx.x]];
+  float s = 0.f;
+  for (int i = threadIdx.x; i < d.ntile_ew; i += 256) s += d.part[i];
+  const float tot = block_sum_256(s, red);
+  if (threadIdx.x == 0) d.stat[0] = 1.0f / (sqrtf(tot) + eps);
+}
+
+}  // namespace
+
+void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, float omb, int nesterov,
+                     hipStream_t s) {
+  if (tm.total == 0) return;
+  if (ns_dt == DT_BF16)
+    hipLaunchKernelGGL(momentum_kernel<uint16_t>, dim3(tm.total), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
+  else
+    hipLaunchKernelGGL(momentum_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
+}
+
+void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, hipStream_t s) {
+  if (tm.total == 0) return;
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(tm.total), dim3(256), 0, s, mats, tm, eps);
+}
+
+}  // namespace ma

@@ -1,0 +1,63 @@
+// Host-side launchers of the Muon / AdamW kernels. Each enqueues on `s`.
+#pragma once
+
+#include "common.hpp"
+
+namespace ma {
+
+// Momentum EMA + Nesterov lerp + canonical-orientation Q write + per-tile
+// Frobenius partials (speedtronic "Muon update", first two lines).
+void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, float one_minus_beta,
+                     int nesterov, hipStream_t s);
+// sigma = 1 / (sqrt(sum of partials) + eps), one block per matrix, fixed order.
+void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, hipStream_t s);
+
+// One product of a Newton-Schulz iteration over every matrix (op 0: Gram
+// A = s2 * X X^T, lower-triangle tiles mirrored; op 1: B = b A + c A A^T, A
+// symmetric; op 2: X' = s1 * (a X + B X)). On the first iteration s2 = sigma^2
+// and s1 = sigma (the normalisation folded in); otherwise both are 1.
+enum : int { NS_GRAM = 0, NS_SQUARE = 1, NS_APPLY = 2 };
+void launch_ns_bf16(int op, const MatDesc* mats, TileMap tm, int src, int first, float a, float b, float c,
+                    hipStream_t s);
+void launch_ns_f32(int op, const MatDesc* mats, TileMap tm, int src, int first, float a, float b, float c,
+                   hipStream_t s);
+
+// Sums of squares of the final Newton-Schulz output along canonical rows
+// (csum_r) or canonical columns (csum_c), optionally weighted by the square
+// of the stored-row factor (Muon+ second stage).
+void launch_canon_rowsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, int weighted,
+                         hipStream_t s);
+void launch_canon_colsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, int weighted,
+                         hipStream_t s);
+// NorMuon: V update and per-stored-row factor d_i * kappa (one block / matrix).
+void launch_finalize_normuon(const MatDesc* mats, TileMap tm, float beta2, hipStream_t s);
+// Muon+: stage 1 row factors 1/sqrt(r_i + eps), stage 2 column factors.
+void launch_finalize_muon_plus(const MatDesc* mats, TileMap tm, int stage, float eps, hipStream_t s);
+
+// Scale + decoupled decay + apply in the stored orientation, with the cautious
+// masks; mode 1 copies U out instead (Newton-Schulz-only entry).
+enum : int { APPLY_UPDATE = 0, APPLY_COPY = 1 };
+void launch_apply(const MatDesc* mats, TileMap tm, int ns_dt, int src, int mode, int cautious,
+                  int use_rfac, int use_cfac, hipStream_t s);
+
+// Multi-tensor AdamW.
+struct AdamTensorArg {
+  void* p;
+  const void* g;
+  float* m;
+  float* v;
+  int64_t numel;
+  int32_t pdt, gdt;
+  float lr, wd;
+};
+constexpr int kMaxAdamTensors = 32;
+constexpr int kAdamChunk = 8192;  // elements per block
+struct AdamLaunch {
+  AdamTensorArg t[kMaxAdamTensors];
+  int32_t block_start[kMaxAdamTensors + 1];
+  int32_t nt;
+  float b1, omb1, b2, omb2, eps, inv_bc1, inv_sqrt_bc2;
+};
+void launch_adamw(const AdamLaunch& L, int nblocks, hipStream_t s);
+
+}  // namespace ma

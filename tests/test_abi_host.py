@@ -1,0 +1,265 @@
+"""The C-ABI library on the host: it loads, exports every declared symbol,
+matches the header's struct layouts, validates arguments without touching the
+GPU, and plans the five parameter sets as expected. No GPU work is enqueued:
+every call here returns before its first HIP call (invalid arguments, missing
+workspace, or an empty step)."""
+import ctypes
+import math
+import os
+import re
+import subprocess
+
+import pytest
+
+import muon_adamw_amd as ma
+import workloads
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "muon_adamw.h")
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(ma.LIB_PATH):
+        from muon_adamw_amd import build
+        build.build()
+    return ma.load_library()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    names = re.findall(r"^\s*(?:const\s+)?[a-z_0-9]+\s*\*?\s*([a-z_0-9]+)\s*\(", text, flags=re.M)
+    return sorted(set(names))
+
+
+def test_exports_every_declared_symbol(lib):
+    names = declared_functions()
+    assert set(names) == set(ma.EXPORTS), names
+    for name in names:
+        assert hasattr(lib, name), name
+    out = subprocess.run(["nm", "-D", "--defined-only", ma.LIB_PATH], capture_output=True, text=True).stdout
+    for name in names:
+        assert re.search(rf" T {name}$", out, flags=re.M), name
+
+
+def test_struct_layouts_match_header(tmp_path):
+    src = tmp_path / "layout.c"
+    src.write_text(f'''
+#include <stdio.h>
+#include <stddef.h>
+#include "{HEADER}"
+#define S(T) printf(#T " %zu\\n", sizeof(T))
+#define O(T, f) printf(#T "." #f " %zu\\n", offsetof(T, f))
+int main(void) {{
+  S(ma_muon_tensor); O(ma_muon_tensor, batch); O(ma_muon_tensor, views); O(ma_muon_tensor, lr);
+  O(ma_muon_tensor, weight_decay);
+  S(ma_muon_hparams); O(ma_muon_hparams, ns_dtype); O(ma_muon_hparams, cautious);
+  S(ma_adamw_tensor); O(ma_adamw_tensor, numel); O(ma_adamw_tensor, weight_decay);
+  S(ma_adamw_hparams); O(ma_adamw_hparams, step);
+  S(ma_matrix_info); O(ma_matrix_info, scale); O(ma_matrix_info, u_offset);
+  return 0;
+}}''')
+    exe = tmp_path / "layout"
+    subprocess.run(["gcc", "-std=c99", str(src), "-o", str(exe)], check=True)
+    got = dict(line.rsplit(" ", 1) for line in subprocess.run([str(exe)], capture_output=True,
+                                                               text=True).stdout.splitlines())
+    want = {
+        "ma_muon_tensor": ctypes.sizeof(ma.MuonTensorC),
+        "ma_muon_tensor.batch": ma.MuonTensorC.batch.offset,
+        "ma_muon_tensor.views": ma.MuonTensorC.views.offset,
+        "ma_muon_tensor.lr": ma.MuonTensorC.lr.offset,
+        "ma_muon_tensor.weight_decay": ma.MuonTensorC.weight_decay.offset,
+        "ma_muon_hparams": ctypes.sizeof(ma.MuonHParamsC),
+        "ma_muon_hparams.ns_dtype": ma.MuonHParamsC.ns_dtype.offset,
+        "ma_muon_hparams.cautious": ma.MuonHParamsC.cautious.offset,
+        "ma_adamw_tensor": ctypes.sizeof(ma.AdamWTensorC),
+        "ma_adamw_tensor.numel": ma.AdamWTensorC.numel.offset,
+        "ma_adamw_tensor.weight_decay": ma.AdamWTensorC.weight_decay.offset,
+        "ma_adamw_hparams": ctypes.sizeof(ma.AdamWHParamsC),
+        "ma_adamw_hparams.step": ma.AdamWHParamsC.step.offset,
+        "ma_matrix_info": ctypes.sizeof(ma.MatrixInfoC),
+        "ma_matrix_info.scale": ma.MatrixInfoC.scale.offset,
+        "ma_matrix_info.u_offset": ma.MatrixInfoC.u_offset.offset,
+    }
+    for k, v in want.items():
+        assert int(got[k]) == v, (k, got[k], v)
+
+
+# ---------------------------------------------------------------------------
+# descriptors with fake, non-overlapping device addresses
+# ---------------------------------------------------------------------------
+BASE = 1 << 40
+
+
+def fake_descs(wl, gap=1 << 34):
+    specs = wl.muon
+    arr = (ma.MuonTensorC * len(specs))()
+    addr = BASE
+    for i, t in enumerate(specs):
+        d = arr[i]
+        es = 2 if t.param_dtype == "bf16" else 4
+        n = t.batch * t.rows * t.cols
+        d.param = addr; addr += n * es + gap
+        d.grad = addr; addr += n * 4 + gap
+        d.momentum = addr; addr += n * 4 + gap
+        d.row_v = addr if wl.muon_hp.normuon else None
+        addr += t.batch * t.rows * 4 + gap
+        d.batch, d.rows, d.cols, d.views = t.batch, t.rows, t.cols, t.views
+        d.param_dtype = ma.MA_BF16 if t.param_dtype == "bf16" else ma.MA_F32
+        d.grad_dtype = ma.MA_BF16 if t.grad_dtype == "bf16" else ma.MA_F32
+        d.lr, d.weight_decay = t.lr, t.wd
+    return arr
+
+
+def hp_of(wl):
+    h = wl.muon_hp
+    return ma.muon_hparams(h.beta, h.nesterov, h.ns_steps, h.ns_coeffs, h.ns_eps, h.ns_dtype, h.normuon,
+                           h.normuon_beta2, h.muon_plus, h.muon_plus_eps, h.cautious)
+
+
+def counts(lib, arr, n, hp):
+    nm, nb = ctypes.c_int32(-1), ctypes.c_int32(-1)
+    st = lib.ma_muon_plan_counts(arr, n, ctypes.byref(hp), ctypes.byref(nm), ctypes.byref(nb))
+    return st, nm.value, nb.value
+
+
+@pytest.mark.parametrize("k,nmat,nbucket", [(1, 1, 1), (2, 72, 2), (3, 56, 3), (4, 192, 1), (5, 24, 2)])
+def test_plan_counts(lib, k, nmat, nbucket):
+    wl = workloads.workload(k)
+    arr = fake_descs(wl)
+    st, nm, nb = counts(lib, arr, len(wl.muon), hp_of(wl))
+    assert st == 0, lib.ma_last_error()
+    assert (nm, nb) == (nmat, nbucket)
+    assert nm == len(wl.matrices())
+
+
+def info(lib, arr, n, hp, k):
+    out = ma.MatrixInfoC()
+    st = lib.ma_muon_matrix_info(arr, n, ctypes.byref(hp), k, ctypes.byref(out))
+    assert st == 0, lib.ma_last_error()
+    return out
+
+
+def test_matrix_info_canonical_shapes(lib):
+    wl = workloads.workload(2)
+    arr, hp = fake_descs(wl), hp_of(wl)
+    up = info(lib, arr, len(wl.muon), hp, 4)          # layer 0 mlp.up 3072x768
+    assert (up.m, up.n, up.r, up.c, up.transposed) == (3072, 768, 768, 3072, 1)
+    assert up.scale == pytest.approx(2.0, abs=0)
+    down = info(lib, arr, len(wl.muon), hp, 5)        # 768x3072
+    assert (down.transposed, down.r, down.c, down.scale) == (0, 768, 3072, 1.0)
+    assert up.bucket == down.bucket
+    wl3 = workloads.workload(3)
+    arr3, hp3 = fake_descs(wl3), hp_of(wl3)
+    gate = info(lib, arr3, len(wl3.muon), hp3, 4)     # first view of l0.gate_up
+    upv = info(lib, arr3, len(wl3.muon), hp3, 5)
+    assert (gate.tensor, gate.view, upv.view) == (4, 0, 1)
+    assert (gate.m, gate.n, gate.r, gate.c, gate.transposed) == (14336, 4096, 4096, 14336, 1)
+    assert gate.scale == pytest.approx(math.sqrt(3.5), rel=1e-7)
+    wl4 = workloads.workload(4)
+    arr4, hp4 = fake_descs(wl4), hp_of(wl4)
+    dn = info(lib, arr4, len(wl4.muon), hp4, 128)     # first expert's down 2048x1408
+    assert (dn.tensor, dn.batch_index, dn.m, dn.n, dn.r, dn.c, dn.rp, dn.cp) == (1, 0, 2048, 1408, 1408,
+                                                                                  2048, 1408, 2048)
+    assert dn.transposed == 1
+
+
+def test_workspace_bytes_cover_buffers(lib):
+    wl = workloads.workload(2)
+    arr, hp = fake_descs(wl), hp_of(wl)
+    need = lib.ma_muon_workspace_bytes(arr, len(wl.muon), ctypes.byref(hp))
+    # two X buffers + A + B per matrix at bf16, at least
+    floor = sum(2 * (2 * m_r * m_c + 2 * m_r * m_r) for (_, _, _, m, n) in wl.matrices()
+                for (m_r, m_c) in [(min(m, n), max(m, n))])
+    assert floor <= need < floor * 1.05
+    last = info(lib, arr, len(wl.muon), hp, 71)
+    assert last.u_offset + last.rp * last.cp * 2 <= need
+
+
+def step(lib, arr, n, hp, ws=None, nbytes=0):
+    return lib.muon_step(arr, n, ctypes.byref(hp), ws, nbytes, None)
+
+
+def test_validation_statuses(lib):
+    wl = workloads.workload(2)
+    n = len(wl.muon)
+    hp = hp_of(wl)
+    # missing workspace
+    assert step(lib, fake_descs(wl), n, hp) == 4
+    assert b"workspace" in lib.ma_last_error()
+    # misaligned workspace
+    assert step(lib, fake_descs(wl), n, hp, ctypes.c_void_p(BASE + 8), 1 << 40) == 4
+    # rows not divisible by views
+    arr = fake_descs(wl); arr[0].views = 5
+    assert step(lib, arr, n, hp) == 1
+    # complex / unknown dtype
+    arr = fake_descs(wl); arr[3].grad_dtype = 9
+    assert step(lib, arr, n, hp) == 2
+    assert b"complex" in lib.ma_last_error()
+    # tied weights passed twice
+    arr = fake_descs(wl); arr[1].param = arr[0].param
+    assert step(lib, arr, n, hp) == 3
+    # momentum overlapping another tensor's parameter
+    arr = fake_descs(wl); arr[2].momentum = arr[1].param + 16
+    assert step(lib, arr, n, hp) == 3
+    # NorMuon and Muon+ together
+    bad = ma.muon_hparams(normuon=True, muon_plus=True)
+    assert step(lib, fake_descs(wl), n, bad) == 5
+    # NorMuon without row_v
+    assert step(lib, fake_descs(wl), n, ma.muon_hparams(normuon=True)) == 1
+    # hyperparameters
+    for kw in [dict(beta=1.0), dict(ns_steps=0), dict(ns_steps=65), dict(cautious="none", ns_eps=-1.0)]:
+        assert step(lib, fake_descs(wl), n, ma.muon_hparams(**kw)) == 1, kw
+    hpn = ma.muon_hparams(); hpn.cautious = 3
+    assert step(lib, fake_descs(wl), n, hpn) == 1
+    hpn = ma.muon_hparams(); hpn.ns_a = float("nan")
+    assert step(lib, fake_descs(wl), n, hpn) == 1
+    # non-finite lr
+    arr = fake_descs(wl); arr[0].lr = float("inf")
+    assert step(lib, arr, n, hp) == 1
+    # null momentum with a gradient
+    arr = fake_descs(wl); arr[0].momentum = None
+    assert step(lib, arr, n, hp) == 1
+
+
+def test_absent_gradients_make_an_empty_step(lib):
+    wl = workloads.workload(2)
+    arr = fake_descs(wl)
+    for i in range(len(wl.muon)):
+        arr[i].grad = None
+        arr[i].momentum = None
+    hp = hp_of(wl)
+    assert counts(lib, arr, len(wl.muon), hp)[1] == 0
+    assert lib.ma_muon_workspace_bytes(arr, len(wl.muon), ctypes.byref(hp)) == 0
+    assert step(lib, arr, len(wl.muon), hp) == 0     # nothing to do, no GPU call
+
+
+def test_adamw_validation(lib):
+    t = (ma.AdamWTensorC * 2)()
+    for i in range(2):
+        t[i].param = BASE + i * (1 << 30)
+        t[i].grad = BASE + (1 << 34) + i * (1 << 30)
+        t[i].m = BASE + (2 << 34) + i * (1 << 30)
+        t[i].v = BASE + (3 << 34) + i * (1 << 30)
+        t[i].numel = 1000
+        t[i].lr, t[i].weight_decay = 3e-4, 0.1
+    good = ma.AdamWHParamsC(0.9, 0.95, 1e-8, 0, 1)
+    assert lib.adamw_step(t, 2, ctypes.byref(ma.AdamWHParamsC(0.9, 0.95, 1e-8, 0, 0)), None) == 1
+    assert lib.adamw_step(t, 2, ctypes.byref(ma.AdamWHParamsC(1.0, 0.95, 1e-8, 0, 1)), None) == 1
+    t[1].param = t[0].param + 400
+    assert lib.adamw_step(t, 2, ctypes.byref(good), None) == 3
+    t[1].param = BASE + (1 << 30)
+    t[1].param_dtype = 4
+    assert lib.adamw_step(t, 2, ctypes.byref(good), None) == 2
+    t[1].param_dtype = 0
+    t[0].grad = None
+    t[1].grad = None
+    assert lib.adamw_step(t, 2, ctypes.byref(good), None) == 0   # nothing to do
+
+
+def test_newton_schulz_workspace_query(lib):
+    hp = ma.muon_hparams(ns_dtype="bf16")
+    assert lib.ma_newton_schulz_workspace_bytes(1, 300, 200, ma.MA_BF16, ctypes.byref(hp)) > 0
+    assert lib.ma_newton_schulz_workspace_bytes(1, 0, 200, ma.MA_BF16, ctypes.byref(hp)) == 0
+    assert lib.ma_newton_schulz(None, None, 1, 4, 4, ma.MA_F32, ctypes.byref(hp), None, 0, None) == 1

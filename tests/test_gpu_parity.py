@@ -1,0 +1,400 @@
+"""HIP path vs the fp64 oracle on the same seeded inputs (needs an MI355X).
+
+Tolerances: fp32 paths 1e-5 relative (Frobenius, per tensor) on updated
+parameters and momentum; bf16 matrix-core Newton-Schulz 2e-2 relative
+Frobenius per matrix against the fp64 oracle; AdamW 1e-6 relative on p, m, v.
+The epilogue is also checked "staged": the oracle's NorMuon / Muon+ / scale /
+decay / cautious steps are fed the GPU's own Newton-Schulz output, and the
+parameters must then agree to fp32 rounding.
+"""
+import math
+
+import numpy as np
+import pytest
+import torch
+
+import muon_adamw_amd as ma
+import workloads
+from oracle import adamw as oadamw
+from oracle import muon as omuon
+from oracle import storage
+from tests.gpu_helpers import (adamw_params, flush, host, hp_c, hp_dict, muon_params, rel, snapshot,
+                               to_gpu)
+
+pytestmark = pytest.mark.gpu
+
+DEV = "cuda"
+
+
+def randn(shape, seed, scale=1.0):
+    g = torch.Generator().manual_seed(seed)
+    return torch.randn(shape, generator=g, dtype=torch.float32) * scale
+
+
+# ---------------------------------------------------------------------------
+# Newton-Schulz alone
+# ---------------------------------------------------------------------------
+F32_SHAPES = [(1, 1), (4, 3), (3, 4), (5, 5), (37, 100), (100, 37), (128, 256), (256, 128), (130, 129),
+              (64, 300), (200, 200)]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_newton_schulz_f32(shape):
+    flush(f"ns f32 {shape}")
+    x = randn(shape, 100 + shape[0] * 7 + shape[1])
+    out = ma.newton_schulz(x.to(DEV), ma.muon_hparams(ns_dtype="f32"))
+    torch.cuda.synchronize()
+    want = omuon.newton_schulz(x.double().numpy())
+    err = rel(out.cpu().double().numpy(), want)
+    # fp32 rounding is amplified by up to phi'(0)^5 = 3.4445^5 ~ 490 on the
+    # smallest singular directions of near-square Gaussian inputs
+    tol = 1e-5 if max(shape) >= 2 * min(shape) else 2e-4
+    assert err < tol, err
+
+
+def test_newton_schulz_f32_well_conditioned():
+    """256x128 with singular values in [0.1, 1] (condition 10): fp32 to 1e-5."""
+    g = torch.Generator().manual_seed(7)
+    U, _ = torch.linalg.qr(torch.randn(256, 128, generator=g, dtype=torch.float64))
+    V, _ = torch.linalg.qr(torch.randn(128, 128, generator=g, dtype=torch.float64))
+    S = torch.logspace(0, -1, 128, dtype=torch.float64)
+    x = ((U * S) @ V.T).float()
+    out = ma.newton_schulz(x.to(DEV), ma.muon_hparams(ns_dtype="f32"))
+    err = rel(out.cpu().double().numpy(), omuon.newton_schulz(x.double().numpy()))
+    assert err < 1e-5, err
+
+
+BF16_SHAPES = [(1, 1), (7, 3), (128, 128), (256, 128), (300, 200), (200, 300), (129, 1000), (768, 768),
+               (768, 3072), (3072, 768), (1408, 2048)]
+
+
+@pytest.mark.parametrize("shape", BF16_SHAPES, ids=lambda s: f"{s[0]}x{s[1]}")
+def test_newton_schulz_bf16(shape):
+    flush(f"ns bf16 {shape}")
+    x = randn(shape, 200 + shape[0] + 3 * shape[1]).to(torch.bfloat16)
+    out = ma.newton_schulz(x.to(DEV), ma.muon_hparams(ns_dtype="bf16"))
+    torch.cuda.synchronize()
+    want = omuon.newton_schulz(host(x))
+    err = rel(host(out), want)
+    assert err < 2e-2, err
+
+
+def test_newton_schulz_batched_bf16():
+    x = randn((3, 300, 200), 5).to(torch.bfloat16)
+    out = ma.newton_schulz(x.to(DEV), ma.muon_hparams(ns_dtype="bf16"))
+    xs, os_ = host(x), host(out)
+    for b in range(3):
+        assert rel(os_[b], omuon.newton_schulz(xs[b])) < 2e-2
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_newton_schulz_transpose_bitwise(dt):
+    """NS(X^T) = NS(X)^T holds bit for bit: a tall input is the same canonical
+    matrix as its wide transpose."""
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    x = randn((200, 520), 11).to(tdt)
+    hp = ma.muon_hparams(ns_dtype=dt)
+    a = ma.newton_schulz(x.to(DEV), hp)
+    b = ma.newton_schulz(x.t().contiguous().to(DEV), hp)
+    assert torch.equal(a.t().contiguous(), b)
+
+
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+def test_newton_schulz_zero_stays_finite(dt):
+    tdt = torch.float32 if dt == "f32" else torch.bfloat16
+    z = torch.zeros((96, 200), dtype=tdt, device=DEV)
+    out = ma.newton_schulz(z, ma.muon_hparams(ns_dtype=dt))
+    assert torch.isfinite(out.float()).all() and (out == 0).all()
+
+
+# ---------------------------------------------------------------------------
+# Whole Muon step
+# ---------------------------------------------------------------------------
+def oracle_inputs(data):
+    """Host copies of every Muon tensor's stored inputs, for the oracle."""
+    out = []
+    for t in data.muon:
+        if t is None:
+            continue
+        out.append({"param": workloads.to_numpy(t.param), "param_dtype": t.spec.param_dtype,
+                    "grad": None if t.grad is None else workloads.to_numpy(t.grad),
+                    "grad_dtype": t.spec.grad_dtype, "momentum": workloads.to_numpy(t.momentum),
+                    "row_v": None if t.row_v is None else workloads.to_numpy(t.row_v),
+                    "views": t.spec.views, "lr": t.spec.lr, "wd": t.spec.wd, "shape": t.spec.shape})
+    return out
+
+
+def check_momentum(gpu_mom, want_f32, tol=1e-5):
+    got = gpu_mom.cpu().double().numpy().ravel()
+    assert rel(got, want_f32.astype(np.float64).ravel()) < tol
+
+
+def test_config1_end_to_end():
+    """One fp32 256x128 tall matrix, fp32 Newton-Schulz: parameters, momentum
+    and the orthogonalised update all within 1e-5 of the fp64 oracle."""
+    wl = workloads.workload(1)
+    data = to_gpu(workloads.generate(wl, device="cpu"))
+    inp = oracle_inputs(data)
+    hp = hp_c(wl.muon_hp)
+    ws = ma.muon_step(muon_params(data), hp)
+    torch.cuda.synchronize()
+    want = omuon.muon_step(inp, hp_dict(wl.muon_hp))[0]
+    t = data.muon[0]
+    assert rel(t.param.cpu().double().numpy(), want["W64"]) < 1e-5
+    check_momentum(t.momentum, want["momentum"])
+    info = ma.matrix_info(muon_params(data), hp, 0)
+    assert info["transposed"] == 1 and abs(info["scale"] - math.sqrt(2)) < 1e-7
+    U = ma.workspace_u(ws, info, "f32").cpu().double().numpy()[: info["r"], : info["c"]]
+    assert rel(U.T, want["U64"][0]) < 1e-5
+    # the update itself, not just the decayed parameters
+    W0 = storage.decode(inp[0]["param"], "f32").reshape(want["W64"].shape)
+    dW_gpu = t.param.cpu().double().numpy() - W0
+    assert rel(dW_gpu, want["W64"] - W0) < 1e-5
+
+
+def staged_apply(W0, U_gpu_stored, G, V0, hp, lr, wd, m, n):
+    """The oracle's post-Newton-Schulz steps fed the GPU's own U."""
+    U = U_gpu_stored
+    V1 = V0
+    if hp["normuon"]:
+        U, V1 = omuon.normuon(U, V0, hp["normuon_beta2"])
+    if hp["muon_plus"]:
+        U = omuon.muon_plus_row_col(U, hp["muon_plus_eps"])
+    s = omuon.shape_scale(m, n)
+    if hp["cautious"] == "none":
+        return omuon.apply_decoupled(W0, U, lr, wd, s), V1
+    if hp["cautious"] == "wd_mask":
+        return omuon.apply_cautious_wd(W0, U, lr, wd, s), V1
+    return omuon.apply_cautious_wrapper(W0, U, G, lr, wd, s)[0], V1
+
+
+def gpu_u_stored(ws, info, ns_dtype):
+    U = ma.workspace_u(ws, info, ns_dtype).cpu().float().double().numpy()[: info["r"], : info["c"]]
+    return U.T if info["transposed"] else U
+
+
+def run_and_check_muon(k, matrix_filter=None, full_oracle_ns=True, tol_ns=2e-2):
+    """Runs a workload's Muon step on the GPU and checks, per matrix: momentum
+    (1e-5), the Newton-Schulz output against the oracle (bf16: 2e-2), and the
+    staged epilogue (parameters to fp32/bf16 rounding given the GPU's U)."""
+    wl = workloads.workload(k) if isinstance(k, int) else k
+    h = hp_dict(wl.muon_hp)
+    data = to_gpu(workloads.generate(wl, device="cpu" if wl.gen_device == "cpu" else DEV))
+    params = muon_params(data)
+    hp = hp_c(wl.muon_hp)
+    before = [(snapshot(t.param), snapshot(t.momentum), snapshot(t.row_v)) for t in data.muon]
+    flush(f"workload {wl.name}: muon_step")
+    ws = ma.muon_step(params, hp)
+    torch.cuda.synchronize()
+    nmat, _ = ma.plan_counts(params, hp)
+    checked = 0
+    for kk in range(nmat):
+        info = ma.matrix_info(params, hp, kk)
+        if matrix_filter is not None and not matrix_filter(kk, info):
+            continue
+        ti, b, v = info["tensor"], info["batch_index"], info["view"]
+        t = data.muon[ti]
+        m, n = info["m"], info["n"]
+        rs = slice(v * m, (v + 1) * m)
+        W0 = host(before[ti][0][b, rs] if t.param.dim() == 3 else before[ti][0][rs])
+        G = host(t.grad[b, rs] if t.grad.dim() == 3 else t.grad[rs])
+        B0 = host(before[ti][1][b, rs] if t.momentum.dim() == 3 else before[ti][1][rs])
+        beta = h["beta"]
+        B1 = omuon.momentum_ema(B0, G, beta)
+        Q = omuon.nesterov_lerp(G, B1, beta)
+        B_gpu = host(t.momentum[b, rs] if t.momentum.dim() == 3 else t.momentum[rs])
+        assert rel(B_gpu, B1) < 1e-5, (kk, "momentum")
+        U_gpu = gpu_u_stored(ws, info, wl.muon_hp.ns_dtype)
+        if full_oracle_ns:
+            U_want = omuon.newton_schulz(Q, h["ns_steps"], h["ns_eps"], h["ns_coeffs"])
+            e = rel(U_gpu, U_want)
+            assert e < tol_ns, (kk, "newton-schulz", e)
+        V0 = None if t.row_v is None else host(before[ti][2][b, rs])
+        W_want, V_want = staged_apply(W0, U_gpu, G, V0, h, t.spec.lr, t.spec.wd, m, n)
+        W_gpu = host(t.param[b, rs] if t.param.dim() == 3 else t.param[rs])
+        if t.spec.param_dtype == "f32":
+            assert rel(W_gpu, W_want) < 1e-5, (kk, "staged apply", rel(W_gpu, W_want))
+            dW = W_gpu - W0
+            assert rel(dW, W_want - W0) < 1e-4, (kk, "staged update")
+        else:
+            bits = workloads.to_numpy(t.param[b, rs] if t.param.dim() == 3 else t.param[rs]).astype(np.int32)
+            want_bits = storage.round_bf16_bits(W_want).astype(np.int32)
+            # within one bf16 ulp, and equal almost everywhere
+            assert np.abs(bits - want_bits).max() <= 1, (kk, "bf16 ulp")
+            assert np.mean(bits != want_bits) < 1e-3, (kk, "bf16 mismatch rate")
+        if V0 is not None:
+            V_gpu = host(t.row_v[b, rs])
+            assert rel(V_gpu, V_want) < 1e-5, (kk, "normuon V")
+        checked += 1
+    assert checked > 0
+    return data, ws
+
+
+def test_config2_muon_full():
+    """GPT 12L d768: all 72 matrices against the oracle."""
+    run_and_check_muon(2)
+
+
+def test_config2_adamw():
+    wl = workloads.workload(2)
+    data = to_gpu(workloads.generate(wl, device="cpu"))
+    before = [(workloads.to_numpy(t.param), workloads.to_numpy(t.grad), workloads.to_numpy(t.m),
+               workloads.to_numpy(t.v)) for t in data.adamw]
+    h = wl.adamw_hp
+    flush("config2 adamw_step")
+    ma.adamw_step(adamw_params(data), h.beta1, h.beta2, h.eps, h.step)
+    torch.cuda.synchronize()
+    tens = [{"param": p, "param_dtype": t.spec.param_dtype, "grad": g, "grad_dtype": t.spec.grad_dtype,
+             "m": m, "v": v, "lr": t.spec.lr, "wd": t.spec.wd}
+            for (p, g, m, v), t in zip(before, data.adamw)]
+    want = oadamw.adamw_step(tens, {"beta1": h.beta1, "beta2": h.beta2, "eps": h.eps, "step": h.step})
+    for t, w in zip(data.adamw, want):
+        assert rel(host(t.param), w["p64"]) < 1e-6
+        assert rel(host(t.m), w["m64"]) < 1e-6
+        assert rel(host(t.v), w["v64"]) < 1e-6
+
+
+def test_adamw_two_steps_bf16_params_and_tail():
+    """bf16 params/grads, a ragged length, two steps; step 2 is checked against
+    the oracle fed the GPU's stored state after step 1."""
+    n = 100003
+    p = randn((n,), 1, 0.02).to(torch.bfloat16)
+    g1 = randn((n,), 2, 1e-3).to(torch.bfloat16)
+    g2 = randn((n,), 3, 1e-3).to(torch.bfloat16)
+    P = ma.AdamWParam(p.to(DEV), g1.to(DEV), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                      1e-3, 0.05)
+    ma.adamw_step([P], 0.9, 0.999, 1e-8, 1)
+    torch.cuda.synchronize()
+    p1, m1, v1 = oadamw.adamw_update(host(p), host(g1), np.zeros(n), np.zeros(n), 1e-3, 0.05, 0.9, 0.999,
+                                     1e-8, 1)
+    assert rel(host(P.m), m1) < 1e-6 and rel(host(P.v), v1) < 1e-6
+    bits = workloads.to_numpy(P.param).astype(np.int32)
+    assert np.abs(bits - storage.round_bf16_bits(p1).astype(np.int32)).max() <= 1
+    p1g, m1g, v1g = host(P.param), host(P.m), host(P.v)
+    P.grad = g2.to(DEV)
+    ma.adamw_step([P], 0.9, 0.999, 1e-8, 2)
+    torch.cuda.synchronize()
+    p2, m2, v2 = oadamw.adamw_update(p1g, host(g2), m1g, v1g, 1e-3, 0.05, 0.9, 0.999, 1e-8, 2)
+    assert rel(host(P.m), m2) < 1e-6 and rel(host(P.v), v2) < 1e-6
+    bits = workloads.to_numpy(P.param).astype(np.int32)
+    assert np.abs(bits - storage.round_bf16_bits(p2).astype(np.int32)).max() <= 1
+
+
+def test_config4_sampled():
+    """MoE 64 experts: NorMuon + cautious weight-decay mask. Every matrix's
+    momentum, V and staged epilogue; Newton-Schulz against the oracle on a
+    sample of gate, up and down matrices."""
+    sample = {0, 1, 77, 128, 191}
+    run_and_check_muon(4, matrix_filter=None, full_oracle_ns=False)
+    run_and_check_muon(4, matrix_filter=lambda kk, info: kk in sample, full_oracle_ns=True)
+
+
+# ---------------------------------------------------------------------------
+# Edge cases of the step
+# ---------------------------------------------------------------------------
+def small_workload(param_dtype="f32", grad_dtype="f32", ns_dtype="bf16", cautious="none", normuon=False,
+                   muon_plus=False):
+    specs = (workloads.MuonTensorSpec("a", 1, 300, 200, param_dtype=param_dtype, grad_dtype=grad_dtype),
+             workloads.MuonTensorSpec("b", 2, 2 * 96, 160, views=2, param_dtype=param_dtype,
+                                      grad_dtype=grad_dtype),
+             workloads.MuonTensorSpec("c", 1, 64, 500, param_dtype=param_dtype, grad_dtype=grad_dtype),
+             workloads.MuonTensorSpec("d", 1, 37, 23, param_dtype=param_dtype, grad_dtype=grad_dtype))
+    hp = workloads.MuonHParams(ns_dtype=ns_dtype, cautious=cautious, normuon=normuon, muon_plus=muon_plus)
+    return workloads.Workload("small", 9, specs, (), hp)
+
+
+@pytest.mark.parametrize("variant", [
+    dict(),
+    dict(ns_dtype="f32"),
+    dict(param_dtype="bf16", grad_dtype="bf16"),
+    dict(cautious="wd_mask", normuon=True),
+    dict(cautious="wrapper", muon_plus=True),
+    dict(cautious="wrapper", muon_plus=True, param_dtype="bf16", grad_dtype="bf16"),
+    dict(cautious="wd_mask", normuon=True, ns_dtype="f32"),
+], ids=lambda d: "-".join(f"{k}={v}" for k, v in d.items()) or "default")
+def test_small_mixed_shapes(variant):
+    """Ragged tall/wide matrices, a batch and views in one call; every matrix
+    against the oracle (fp32 Newton-Schulz: 1e-4 for these Gaussian, partly
+    near-square inputs; bf16: 2e-2)."""
+    wl = small_workload(**variant)
+    run_and_check_muon(wl, tol_ns=1e-4 if wl.muon_hp.ns_dtype == "f32" else 2e-2)
+
+
+def test_small_f32_end_to_end():
+    """fp32 Newton-Schulz: the whole step (not staged) within 1e-5 of the
+    oracle on tall, wide and packed matrices with aspect ratio >= 1.5."""
+    specs = (workloads.MuonTensorSpec("a", 1, 384, 128),
+             workloads.MuonTensorSpec("b", 2, 2 * 64, 160, views=2),
+             workloads.MuonTensorSpec("c", 1, 64, 500))
+    wl = workloads.Workload("small_f32", 21, specs, (), workloads.MuonHParams(ns_dtype="f32"))
+    data = to_gpu(workloads.generate(wl, device="cpu"))
+    inp = oracle_inputs(data)
+    ma.muon_step(muon_params(data), hp_c(wl.muon_hp))
+    torch.cuda.synchronize()
+    want = omuon.muon_step(inp, hp_dict(wl.muon_hp))
+    for t, w, i in zip(data.muon, want, inp):
+        W0 = storage.decode(i["param"], "f32").reshape(w["W64"].shape)
+        assert rel(host(t.param), w["W64"]) < 1e-5
+        assert rel(host(t.param) - W0, w["W64"] - W0) < 1e-5
+        check_momentum(t.momentum, w["momentum"])
+
+
+def test_absent_gradient_and_zero_gradient():
+    wl = small_workload()
+    data = to_gpu(workloads.generate(wl, device="cpu"))
+    data.muon[1].grad = None                         # inactive expert
+    data.muon[2].grad = torch.zeros_like(data.muon[2].grad)
+    keep_p, keep_m = data.muon[1].param.clone(), data.muon[1].momentum.clone()
+    p2 = data.muon[2].param.clone()
+    ma.muon_step(muon_params(data), hp_c(wl.muon_hp))
+    torch.cuda.synchronize()
+    assert torch.equal(data.muon[1].param, keep_p) and torch.equal(data.muon[1].momentum, keep_m)
+    decay = torch.tensor(1.0 - 0.02 * 0.1, dtype=torch.float64).float().item()
+    assert torch.equal(data.muon[2].param, p2 * decay)
+    assert (data.muon[2].momentum == 0).all()
+    assert not torch.equal(data.muon[0].param, data.muon[0].param * 0)
+
+
+def test_views_match_separate_tensors_bitwise():
+    """A (2, m, n) packed parameter steps exactly like its two halves passed
+    as separate tensors."""
+    g = torch.Generator().manual_seed(3)
+    P = (torch.randn(1, 2 * 96, 160, generator=g) * 0.02).to(DEV)
+    G = torch.randn(1, 2 * 96, 160, generator=g).to(DEV)
+    M = torch.zeros_like(P)
+    P2, M2 = P.clone(), M.clone()
+    hp = ma.muon_hparams()
+    ma.muon_step([ma.MuonParam(P, G, M, views=2)], hp)
+    halves = [ma.MuonParam(P2[:, :96].contiguous(), G[:, :96].contiguous(), M2[:, :96].contiguous()),
+              ma.MuonParam(P2[:, 96:].contiguous(), G[:, 96:].contiguous(), M2[:, 96:].contiguous())]
+    ma.muon_step(halves, hp)
+    torch.cuda.synchronize()
+    assert torch.equal(P[:, :96], halves[0].param) and torch.equal(P[:, 96:], halves[1].param)
+    assert torch.equal(M[:, :96], halves[0].momentum)
+
+
+def test_two_steps_continue_from_state():
+    """Step, then step again: equals the oracle's second step fed the GPU's
+    state after the first; and saving/restoring the state in between changes
+    nothing (bitwise)."""
+    wl = small_workload(ns_dtype="f32")
+    h = hp_dict(wl.muon_hp)
+    data = to_gpu(workloads.generate(wl, device="cpu"))
+    hp = hp_c(wl.muon_hp)
+    ma.muon_step(muon_params(data), hp)
+    torch.cuda.synchronize()
+    saved = [(t.param.cpu().clone(), t.momentum.cpu().clone()) for t in data.muon]
+    for t in data.muon:
+        t.grad = torch.randn(t.grad.shape, generator=torch.Generator().manual_seed(99)).to(DEV)
+    inp = oracle_inputs(data)
+    # a copy restored from host state
+    clone = [ma.MuonParam(p.to(DEV), t.grad, m.to(DEV), None, t.spec.views, t.spec.lr, t.spec.wd)
+             for (p, m), t in zip(saved, data.muon)]
+    ma.muon_step(muon_params(data), hp)
+    ma.muon_step(clone, hp)
+    torch.cuda.synchronize()
+    want = omuon.muon_step(inp, h)
+    for t, c, w in zip(data.muon, clone, want):
+        assert torch.equal(t.param, c.param) and torch.equal(t.momentum, c.momentum)
+        check_momentum(t.momentum, w["momentum"])
+        assert rel(host(t.param), w["W64"]) < 1e-5
