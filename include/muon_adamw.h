@@ -118,19 +118,21 @@ typedef struct {
  * view's stored shape, subject to the cautious mask.
  */
 typedef struct {
-  float beta;
-  int32_t nesterov;
-  int32_t ns_steps;
+  double beta;           /* doubles: the host forms 1 - beta exactly (beta2 = 0.999
+                            as a float would put a 1.3e-5 error into 1 - beta2) */
+  double normuon_beta2;
   float ns_a;
   float ns_b;
   float ns_c;
   float ns_eps;
+  float muon_plus_eps;
+  int32_t nesterov;
+  int32_t ns_steps;
   int32_t ns_dtype;
   int32_t normuon;
-  float normuon_beta2;
   int32_t muon_plus;
-  float muon_plus_eps;
   int32_t cautious;
+  int32_t pad_;
 } ma_muon_hparams;
 
 /* Device bytes of workspace muon_step needs for this tensor list (host call,
@@ -175,10 +177,9 @@ typedef struct {
  * step >= 1 counts successful updates (the caller's host counter).
  */
 typedef struct {
-  float beta1;
-  float beta2;
-  float eps;
-  int32_t pad_;
+  double beta1;
+  double beta2;
+  double eps;
   int64_t step;
 } ma_adamw_hparams;
 

@@ -35,12 +35,13 @@ class MuonTensorC(ctypes.Structure):
 
 
 class MuonHParamsC(ctypes.Structure):
-    _fields_ = [("beta", ctypes.c_float), ("nesterov", ctypes.c_int32),
-                ("ns_steps", ctypes.c_int32), ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float),
-                ("ns_c", ctypes.c_float), ("ns_eps", ctypes.c_float), ("ns_dtype", ctypes.c_int32),
-                ("normuon", ctypes.c_int32), ("normuon_beta2", ctypes.c_float),
-                ("muon_plus", ctypes.c_int32), ("muon_plus_eps", ctypes.c_float),
-                ("cautious", ctypes.c_int32)]
+    _fields_ = [("beta", ctypes.c_double), ("normuon_beta2", ctypes.c_double),
+                ("ns_a", ctypes.c_float), ("ns_b", ctypes.c_float), ("ns_c", ctypes.c_float),
+                ("ns_eps", ctypes.c_float), ("muon_plus_eps", ctypes.c_float),
+                ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
+                ("ns_dtype", ctypes.c_int32), ("normuon", ctypes.c_int32),
+                ("muon_plus", ctypes.c_int32), ("cautious", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
 
 
 class AdamWTensorC(ctypes.Structure):
@@ -51,8 +52,8 @@ class AdamWTensorC(ctypes.Structure):
 
 
 class AdamWHParamsC(ctypes.Structure):
-    _fields_ = [("beta1", ctypes.c_float), ("beta2", ctypes.c_float), ("eps", ctypes.c_float),
-                ("pad_", ctypes.c_int32), ("step", ctypes.c_int64)]
+    _fields_ = [("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
+                ("step", ctypes.c_int64)]
 
 
 class MatrixInfoC(ctypes.Structure):
@@ -170,9 +171,13 @@ def muon_hparams(beta=0.95, nesterov=True, ns_steps=5, ns_coeffs=NS_COEFFS, ns_e
                  ns_dtype="bf16", normuon=False, normuon_beta2=0.95, muon_plus=False,
                  muon_plus_eps=1e-8, cautious="none") -> MuonHParamsC:
     a, b, c = ns_coeffs
-    return MuonHParamsC(beta, int(bool(nesterov)), int(ns_steps), a, b, c, ns_eps,
-                        MA_BF16 if ns_dtype == "bf16" else MA_F32, int(bool(normuon)), normuon_beta2,
-                        int(bool(muon_plus)), muon_plus_eps, CAUTIOUS[cautious])
+    h = MuonHParamsC()
+    h.beta, h.normuon_beta2 = beta, normuon_beta2
+    h.ns_a, h.ns_b, h.ns_c, h.ns_eps, h.muon_plus_eps = a, b, c, ns_eps, muon_plus_eps
+    h.nesterov, h.ns_steps = int(bool(nesterov)), int(ns_steps)
+    h.ns_dtype = MA_BF16 if ns_dtype == "bf16" else MA_F32
+    h.normuon, h.muon_plus, h.cautious = int(bool(normuon)), int(bool(muon_plus)), CAUTIOUS[cautious]
+    return h
 
 
 def _muon_descs(tensors: Sequence[MuonParam], check_device=True):
@@ -268,7 +273,7 @@ def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, s
         else:
             d.grad, d.grad_dtype = None, d.param_dtype
         d.lr, d.weight_decay = t.lr, t.weight_decay
-    hp = AdamWHParamsC(beta1, beta2, eps, 0, int(step))
+    hp = AdamWHParamsC(beta1, beta2, eps, int(step))
     _check(lib.adamw_step(arr, len(tensors), ctypes.byref(hp),
                           ctypes.c_void_p(_stream_handle(stream, device or torch.device("cuda")))))
 

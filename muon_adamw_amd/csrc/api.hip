@@ -92,7 +92,7 @@ MapRef add_map(Plan& P, std::vector<Item> items) {
 
 ma_status validate_hparams(const ma_muon_hparams* hp) {
   if (!hp) return fail(MA_E_INVALID, "hparams is NULL");
-  if (!(hp->beta >= 0.f && hp->beta < 1.f)) return fail(MA_E_INVALID, "beta must be in [0, 1)");
+  if (!(hp->beta >= 0.0 && hp->beta < 1.0)) return fail(MA_E_INVALID, "beta must be in [0, 1)");
   if (hp->nesterov != 0 && hp->nesterov != 1) return fail(MA_E_INVALID, "nesterov must be 0 or 1");
   if (hp->ns_steps < 1 || hp->ns_steps > 64) return fail(MA_E_INVALID, "ns_steps must be in [1, 64]");
   if (!std::isfinite(hp->ns_a) || !std::isfinite(hp->ns_b) || !std::isfinite(hp->ns_c))
@@ -103,7 +103,7 @@ ma_status validate_hparams(const ma_muon_hparams* hp) {
   if (hp->muon_plus != 0 && hp->muon_plus != 1) return fail(MA_E_INVALID, "muon_plus must be 0 or 1");
   if (hp->normuon && hp->muon_plus)
     return fail(MA_E_UNSUPPORTED, "NorMuon and Muon+ together are not defined; enable one");
-  if (hp->normuon && !(hp->normuon_beta2 >= 0.f && hp->normuon_beta2 <= 1.f))
+  if (hp->normuon && !(hp->normuon_beta2 >= 0.0 && hp->normuon_beta2 <= 1.0))
     return fail(MA_E_INVALID, "normuon_beta2 must be in [0, 1]");
   if (hp->muon_plus && !(hp->muon_plus_eps >= 0.f && std::isfinite(hp->muon_plus_eps)))
     return fail(MA_E_INVALID, "muon_plus_eps must be finite and >= 0");
@@ -404,8 +404,8 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
 
   const MatDesc* mats = reinterpret_cast<const MatDesc*>(base);
   auto TM = [&](const MapRef& r) { return device_map(r, base, P.desc_bytes); };
-  const float beta = hp->beta;
-  const float omb = static_cast<float>(1.0 - static_cast<double>(hp->beta));
+  const float beta = static_cast<float>(hp->beta);
+  const float omb = static_cast<float>(1.0 - hp->beta);
   (void)hipGetLastError();
   const int ew_dt = P.ns_dt;
   timed("momentum", s, [&] { launch_momentum(mats, TM(P.ew), ew_dt, beta, omb, hp->nesterov, s); });
@@ -431,7 +431,7 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
     if (P.cols_t.nmat) timed("colsum", s, [&] { launch_canon_colsum(mats, TM(P.cols_t), P.ns_dt, src, 0, s); });
   }
   if (!ns_only && hp->normuon) {
-    timed("finalize_normuon", s, [&] { launch_finalize_normuon(mats, TM(P.fin_all), hp->normuon_beta2, s); });
+    timed("finalize_normuon", s, [&] { launch_finalize_normuon(mats, TM(P.fin_all), static_cast<float>(1.0 - hp->normuon_beta2), s); });
     use_rf = 1;
   }
   if (!ns_only && hp->muon_plus) {
@@ -620,9 +620,9 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
   if (!hp) return fail(MA_E_INVALID, "hparams is NULL");
   if (n < 0) return fail(MA_E_INVALID, "tensor count is negative");
   if (n > 0 && !tensors) return fail(MA_E_INVALID, "tensor array is NULL");
-  if (!(hp->beta1 >= 0.f && hp->beta1 < 1.f) || !(hp->beta2 >= 0.f && hp->beta2 < 1.f))
+  if (!(hp->beta1 >= 0.0 && hp->beta1 < 1.0) || !(hp->beta2 >= 0.0 && hp->beta2 < 1.0))
     return fail(MA_E_INVALID, "betas must be in [0, 1)");
-  if (!(hp->eps >= 0.f) || !std::isfinite(hp->eps)) return fail(MA_E_INVALID, "eps must be finite and >= 0");
+  if (!(hp->eps >= 0.0) || !std::isfinite(hp->eps)) return fail(MA_E_INVALID, "eps must be finite and >= 0");
   if (hp->step < 1) return fail(MA_E_INVALID, "step must be >= 1");
   std::vector<Range> ranges;
   for (int i = 0; i < n; ++i) {
@@ -652,11 +652,11 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
 
   AdamLaunch L{};
   const double b1 = hp->beta1, b2 = hp->beta2;
-  L.b1 = hp->beta1;
+  L.b1 = static_cast<float>(b1);
   L.omb1 = static_cast<float>(1.0 - b1);
-  L.b2 = hp->beta2;
+  L.b2 = static_cast<float>(b2);
   L.omb2 = static_cast<float>(1.0 - b2);
-  L.eps = hp->eps;
+  L.eps = static_cast<float>(hp->eps);
   L.inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(b1, static_cast<double>(hp->step))));
   L.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(b2, static_cast<double>(hp->step))));
   hipStream_t s = static_cast<hipStream_t>(stream);

@@ -55,57 +55,80 @@ __device__ __forceinline__ void tri_decode(int k, int& ti, int& tj) {
   tj = k - i * (i + 1) / 2;
 }
 
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+
+// 16-byte load through a global-address-space pointer (a plain generic
+// pointer would become a flat load, which also counts against the LDS
+// counter and forces early waits).
+__device__ __forceinline__ u32x4 gload16(const uint16_t* p) { return *(g_u32x4*)(p); }
+
+// Operand staging registers for one 64-deep stage: four 16-byte chunks.
+struct Stage4 {
+  u32x4 v0, v1, v2, v3;
+};
+
 // 128 rows x 64 k of a row-major matrix, contraction contiguous.
-__device__ __forceinline__ void load_nt(uint4 (&r)[4], const uint16_t* base, int ld, int k0) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int q = threadIdx.x + 256 * p, row = q >> 3, kc = (q & 7) * 8;
-    r[p] = *reinterpret_cast<const uint4*>(base + (int64_t)row * ld + k0 + kc);
-  }
+__device__ __forceinline__ Stage4 load_nt(const uint16_t* base, int ld, int k0) {
+  const int q = threadIdx.x, row = q >> 3, kc = (q & 7) * 8;
+  const uint16_t* p = base + (int64_t)row * ld + k0 + kc;
+  const int64_t step = (int64_t)32 * ld;   // 256 threads cover 32 rows per chunk
+  Stage4 r;
+  r.v0 = gload16(p);
+  r.v1 = gload16(p + step);
+  r.v2 = gload16(p + 2 * step);
+  r.v3 = gload16(p + 3 * step);
+  return r;
 }
-__device__ __forceinline__ void store_nt(uint16_t* sm, const uint4 (&r)[4]) {
-#pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int q = threadIdx.x + 256 * p, row = q >> 3, kc = (q & 7) * 8;
-    *reinterpret_cast<uint4*>(sm + row * LDA + kc) = r[p];
-  }
+__device__ __forceinline__ void store_nt(uint16_t* sm, const Stage4& r) {
+  const int q = threadIdx.x, row = q >> 3, kc = (q & 7) * 8;
+  uint16_t* p = sm + row * LDA + kc;
+  *reinterpret_cast<u32x4*>(p) = r.v0;
+  *reinterpret_cast<u32x4*>(p + 32 * LDA) = r.v1;
+  *reinterpret_cast<u32x4*>(p + 64 * LDA) = r.v2;
+  *reinterpret_cast<u32x4*>(p + 96 * LDA) = r.v3;
 }
 // 64 k-rows x 128 columns of a row-major matrix (columns contiguous), to be
 // stored transposed (column-major in k) in LDS. Each thread owns 4 k-rows x 8
 // columns.
-__device__ __forceinline__ void load_nn(uint4 (&r)[4], const uint16_t* base, int ld, int k0) {
+__device__ __forceinline__ Stage4 load_nn(const uint16_t* base, int ld, int k0) {
+  const int kq = threadIdx.x & 15, nc = threadIdx.x >> 4;
+  const uint16_t* p = base + (int64_t)(k0 + kq * 4) * ld + nc * 8;
+  Stage4 r;
+  r.v0 = gload16(p);
+  r.v1 = gload16(p + ld);
+  r.v2 = gload16(p + 2 * ld);
+  r.v3 = gload16(p + 3 * ld);
+  return r;
+}
+__device__ __forceinline__ void store_nn(uint16_t* sm, const Stage4& r) {
   const int kq = threadIdx.x & 15, nc = threadIdx.x >> 4;
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    r[i] = *reinterpret_cast<const uint4*>(base + (int64_t)(k0 + kq * 4 + i) * ld + nc * 8);
-}
-__device__ __forceinline__ uint32_t word_of(const uint4& v, int w) {
-  return w == 0 ? v.x : (w == 1 ? v.y : (w == 2 ? v.z : v.w));
-}
-__device__ __forceinline__ void store_nn(uint16_t* sm, const uint4 (&r)[4]) {
-  const int kq = threadIdx.x & 15, nc = threadIdx.x >> 4;
-#pragma unroll
-  for (int e = 0; e < 8; ++e) {
-    const int w = e >> 1, sh = (e & 1) * 16;
-    const uint32_t h0 = (word_of(r[0], w) >> sh) & 0xffffu;
-    const uint32_t h1 = (word_of(r[1], w) >> sh) & 0xffffu;
-    const uint32_t h2 = (word_of(r[2], w) >> sh) & 0xffffu;
-    const uint32_t h3 = (word_of(r[3], w) >> sh) & 0xffffu;
-    uint2 o;
-    o.x = h0 | (h1 << 16);
-    o.y = h2 | (h3 << 16);
-    *reinterpret_cast<uint2*>(sm + (nc * 8 + e) * LDA + kq * 4) = o;
+  for (int w = 0; w < 4; ++w) {
+    const uint32_t a = r.v0[w], b = r.v1[w], c = r.v2[w], d = r.v3[w];
+    // columns 2w and 2w+1 of the four k-rows
+    u32x2 lo, hi;
+    lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);   // (a.lo, b.lo)
+    lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);   // (c.lo, d.lo)
+    hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);   // (a.hi, b.hi)
+    hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);   // (c.hi, d.hi)
+    *reinterpret_cast<u32x2*>(sm + (nc * 8 + 2 * w) * LDA + kq * 4) = lo;
+    *reinterpret_cast<u32x2*>(sm + (nc * 8 + 2 * w + 1) * LDA + kq * 4) = hi;
   }
 }
 
-__device__ __forceinline__ void unpack8(const uint4& v, float* f) {
+typedef __attribute__((address_space(1))) u32x4 g_u32x4_w;
+__device__ __forceinline__ void gstore16(uint16_t* p, u32x4 v) { *(g_u32x4_w*)(p) = v; }
+
+__device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
   f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
   f[4] = __uint_as_float(v.z << 16); f[5] = __uint_as_float(v.z & 0xffff0000u);
   f[6] = __uint_as_float(v.w << 16); f[7] = __uint_as_float(v.w & 0xffff0000u);
 }
-__device__ __forceinline__ uint4 pack8(const float* f) {
-  uint4 v;
+__device__ __forceinline__ u32x4 pack8(const float* f) {
+  u32x4 v;
   v.x = pack_bf16x2(f[0], f[1]);
   v.y = pack_bf16x2(f[2], f[3]);
   v.z = pack_bf16x2(f[4], f[5]);
@@ -155,9 +178,8 @@ __global__ __launch_bounds__(256, 2) void ns_mfma_kernel(NsArgs args) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  uint4 ra[4], rb[4];
-  load_nt(ra, Aop, lda, 0);
-  if (OP == OP_APPLY) load_nn(rb, Bop, ldb, 0); else load_nt(rb, Bop, ldb, 0);
+  Stage4 ra = load_nt(Aop, lda, 0);
+  Stage4 rb = (OP == OP_APPLY) ? load_nn(Bop, ldb, 0) : load_nt(Bop, ldb, 0);
   store_nt(smem, ra);
   if (OP == OP_APPLY) store_nn(smem + OPS, rb); else store_nt(smem + OPS, rb);
   __syncthreads();
@@ -167,8 +189,8 @@ __global__ __launch_bounds__(256, 2) void ns_mfma_kernel(NsArgs args) {
     const int cur = kt & 1;
     const bool more = kt + 1 < nk;
     if (more) {
-      load_nt(ra, Aop, lda, (kt + 1) * BK);
-      if (OP == OP_APPLY) load_nn(rb, Bop, ldb, (kt + 1) * BK); else load_nt(rb, Bop, ldb, (kt + 1) * BK);
+      ra = load_nt(Aop, lda, (kt + 1) * BK);
+      rb = (OP == OP_APPLY) ? load_nn(Bop, ldb, (kt + 1) * BK) : load_nt(Bop, ldb, (kt + 1) * BK);
     }
     const uint16_t* As = smem + cur * 2 * OPS;
     const uint16_t* Bs = As + OPS;
@@ -236,7 +258,7 @@ __global__ __launch_bounds__(256, 2) void ns_mfma_kernel(NsArgs args) {
       for (int u = 0; u < 8; ++u) v[u] *= alpha;
     } else {
       float x[8];
-      unpack8(*reinterpret_cast<const uint4*>(extra + go), x);
+      unpack8(gload16(extra + go), x);
       if (OP == OP_SQUARE) {
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = args.b * x[u] + args.c * v[u];
@@ -245,7 +267,7 @@ __global__ __launch_bounds__(256, 2) void ns_mfma_kernel(NsArgs args) {
         for (int u = 0; u < 8; ++u) v[u] = alpha * (args.a * x[u] + v[u]);
       }
     }
-    *reinterpret_cast<uint4*>(out + go) = pack8(v);
+    gstore16(out + go, pack8(v));
   }
   if (OP != OP_APPLY && ti != tj) {
     // mirrored tile (tj, ti): element (r', c') = C(c', r')
@@ -261,11 +283,11 @@ __global__ __launch_bounds__(256, 2) void ns_mfma_kernel(NsArgs args) {
         for (int u = 0; u < 8; ++u) v[u] *= alpha;
       } else {
         float x[8];
-        unpack8(*reinterpret_cast<const uint4*>(extra + go), x);
+        unpack8(gload16(extra + go), x);
 #pragma unroll
         for (int u = 0; u < 8; ++u) v[u] = args.b * x[u] + args.c * v[u];
       }
-      *reinterpret_cast<uint4*>(out + go) = pack8(v);
+      gstore16(out + go, pack8(v));
     }
   }
 }

@@ -97,12 +97,11 @@ __device__ __forceinline__ float block_sum_256(float v, float* red) {
 // V_i <- V_i + (1 - beta2)(rho_i - V_i); d_i = max(V_i, 1e-30)^-1/2;
 // kappa = ||U||_F / max(||diag(d) U||_F, 1e-30); rfac_i = d_i kappa.
 __global__ __launch_bounds__(256) void finalize_normuon_kernel(const MatDesc* __restrict__ mats, TileMap tm,
-                                                               float beta2) {
+                                                               float omb2) {
   __shared__ float red[4];
   const MatDesc& d = mats[tm.perm[blockIdx.x]];
   const float* rs = d.tall ? d.csum_c : d.csum_r;
   const float inv_n = 1.0f / static_cast<float>(d.n);
-  const float omb2 = 1.0f - beta2;
   float tot = 0.f, toth = 0.f;
   for (int i = threadIdx.x; i < d.m; i += 256) {
     const float s = rs[i];
@@ -153,9 +152,9 @@ void launch_canon_colsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, in
     hipLaunchKernelGGL(canon_colsum_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, weighted);
 }
 
-void launch_finalize_normuon(const MatDesc* mats, TileMap tm, float beta2, hipStream_t s) {
+void launch_finalize_normuon(const MatDesc* mats, TileMap tm, float one_minus_beta2, hipStream_t s) {
   if (tm.total == 0) return;
-  hipLaunchKernelGGL(finalize_normuon_kernel, dim3(tm.total), dim3(256), 0, s, mats, tm, beta2);
+  hipLaunchKernelGGL(finalize_normuon_kernel, dim3(tm.total), dim3(256), 0, s, mats, tm, one_minus_beta2);
 }
 
 void launch_finalize_muon_plus(const MatDesc* mats, TileMap tm, int stage, float eps, hipStream_t s) {

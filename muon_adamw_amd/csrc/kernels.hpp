@@ -30,7 +30,7 @@ void launch_canon_rowsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, in
 void launch_canon_colsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, int weighted,
                          hipStream_t s);
 // NorMuon: V update and per-stored-row factor d_i * kappa (one block / matrix).
-void launch_finalize_normuon(const MatDesc* mats, TileMap tm, float beta2, hipStream_t s);
+void launch_finalize_normuon(const MatDesc* mats, TileMap tm, float one_minus_beta2, hipStream_t s);
 // Muon+: stage 1 row factors 1/sqrt(r_i + eps), stage 2 column factors.
 void launch_finalize_muon_plus(const MatDesc* mats, TileMap tm, int stage, float eps, hipStream_t s);
 

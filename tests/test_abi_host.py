@@ -54,7 +54,7 @@ def test_struct_layouts_match_header(tmp_path):
 int main(void) {{
   S(ma_muon_tensor); O(ma_muon_tensor, batch); O(ma_muon_tensor, views); O(ma_muon_tensor, lr);
   O(ma_muon_tensor, weight_decay);
-  S(ma_muon_hparams); O(ma_muon_hparams, ns_dtype); O(ma_muon_hparams, cautious);
+  S(ma_muon_hparams); O(ma_muon_hparams, normuon_beta2); O(ma_muon_hparams, ns_dtype); O(ma_muon_hparams, cautious);
   S(ma_adamw_tensor); O(ma_adamw_tensor, numel); O(ma_adamw_tensor, weight_decay);
   S(ma_adamw_hparams); O(ma_adamw_hparams, step);
   S(ma_matrix_info); O(ma_matrix_info, scale); O(ma_matrix_info, u_offset);
@@ -71,6 +71,7 @@ int main(void) {{
         "ma_muon_tensor.lr": ma.MuonTensorC.lr.offset,
         "ma_muon_tensor.weight_decay": ma.MuonTensorC.weight_decay.offset,
         "ma_muon_hparams": ctypes.sizeof(ma.MuonHParamsC),
+        "ma_muon_hparams.normuon_beta2": ma.MuonHParamsC.normuon_beta2.offset,
         "ma_muon_hparams.ns_dtype": ma.MuonHParamsC.ns_dtype.offset,
         "ma_muon_hparams.cautious": ma.MuonHParamsC.cautious.offset,
         "ma_adamw_tensor": ctypes.sizeof(ma.AdamWTensorC),
@@ -244,9 +245,9 @@ def test_adamw_validation(lib):
         t[i].v = BASE + (3 << 34) + i * (1 << 30)
         t[i].numel = 1000
         t[i].lr, t[i].weight_decay = 3e-4, 0.1
-    good = ma.AdamWHParamsC(0.9, 0.95, 1e-8, 0, 1)
-    assert lib.adamw_step(t, 2, ctypes.byref(ma.AdamWHParamsC(0.9, 0.95, 1e-8, 0, 0)), None) == 1
-    assert lib.adamw_step(t, 2, ctypes.byref(ma.AdamWHParamsC(1.0, 0.95, 1e-8, 0, 1)), None) == 1
+    good = ma.AdamWHParamsC(0.9, 0.95, 1e-8, 1)
+    assert lib.adamw_step(t, 2, ctypes.byref(ma.AdamWHParamsC(0.9, 0.95, 1e-8, 0)), None) == 1
+    assert lib.adamw_step(t, 2, ctypes.byref(ma.AdamWHParamsC(1.0, 0.95, 1e-8, 1)), None) == 1
     t[1].param = t[0].param + 400
     assert lib.adamw_step(t, 2, ctypes.byref(good), None) == 3
     t[1].param = BASE + (1 << 30)
