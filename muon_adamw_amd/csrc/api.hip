@@ -54,7 +54,9 @@ struct MatPlan {
 
 struct MapRef {
   size_t start_off = 0, perm_off = 0;  // byte offsets inside the table region
-  int nmat = 0, total = 0;
+  int nmat = 0, total = 0, grid = 0, xcd = 0;
+  int xbase[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int xcnt[8] = {0, 0, 0, 0, 0, 0, 0, 0};
 };
 
 struct Plan {
@@ -64,29 +66,70 @@ struct Plan {
   int gemm_tile = 128;
   std::vector<int32_t> ints;
   size_t desc_bytes = 0, table_bytes = 0, ws_bytes = 0;
-  MapRef ew, perm1, sym, app, rows_nt, cols_t, rows_t, cols_nt, fin_all, out;
+  MapRef ew, gram, sq, app, rows_nt, cols_t, rows_t, cols_nt, fin_all, out;
 };
 
 struct Item {
   int mat;
   int tiles;
-  int64_t key;  // larger first
+  int64_t key;  // per-tile work; larger first
 };
 
-MapRef add_map(Plan& P, std::vector<Item> items) {
-  std::stable_sort(items.begin(), items.end(), [](const Item& x, const Item& y) { return x.key > y.key; });
+constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+
+// Lays out a launch's tile list. Plain maps keep one list ordered by
+// decreasing per-tile work (the dispatcher then runs longest tiles first).
+// XCD-aware maps first deal whole matrices to the 8 XCDs, longest total work
+// first onto the least-loaded XCD, then order each XCD's list the same way.
+MapRef add_map(Plan& P, std::vector<Item> items, bool xcd_aware = false) {
+  auto by_key = [](const Item& x, const Item& y) { return x.key > y.key; };
+  std::stable_sort(items.begin(), items.end(), by_key);
   MapRef r;
   r.nmat = static_cast<int>(items.size());
+  std::vector<Item> order;
+  if (xcd_aware && !items.empty()) {
+    std::vector<Item> byw = items;
+    std::stable_sort(byw.begin(), byw.end(), [](const Item& x, const Item& y) {
+      return x.key * x.tiles > y.key * y.tiles;
+    });
+    std::vector<std::vector<Item>> bin(kXcds);
+    int64_t load[kXcds] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (const Item& it : byw) {
+      int b = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < load[b]) b = x;
+      bin[b].push_back(it);
+      load[b] += it.key * it.tiles;
+    }
+    int64_t base = 0, maxc = 0;
+    for (int x = 0; x < kXcds; ++x) {
+      std::stable_sort(bin[x].begin(), bin[x].end(), by_key);
+      int64_t c = 0;
+      for (const Item& it : bin[x]) {
+        order.push_back(it);
+        c += it.tiles;
+      }
+      r.xbase[x] = static_cast<int>(base);
+      r.xcnt[x] = static_cast<int>(c);
+      base += c;
+      maxc = std::max(maxc, c);
+    }
+    r.xcd = 1;
+    r.grid = static_cast<int>(maxc * kXcds);
+  } else {
+    order = items;
+  }
   r.start_off = P.ints.size() * sizeof(int32_t);
   int64_t acc = 0;
-  for (const Item& it : items) {
+  for (const Item& it : order) {
     P.ints.push_back(static_cast<int32_t>(acc));
     acc += it.tiles;
   }
   P.ints.push_back(static_cast<int32_t>(acc));
   r.perm_off = P.ints.size() * sizeof(int32_t);
-  for (const Item& it : items) P.ints.push_back(it.mat);
+  for (const Item& it : order) P.ints.push_back(it.mat);
   r.total = static_cast<int>(acc);
+  if (!r.xcd) r.grid = r.total;
   return r;
 }
 
@@ -138,7 +181,7 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
   if (n > 0 && !t) return fail(MA_E_INVALID, "tensor array is NULL");
   P = Plan();
   P.ns_dt = hp->ns_dtype;
-  P.gemm_tile = hp->ns_dtype == MA_BF16 ? 128 : 64;
+  P.gemm_tile = hp->ns_dtype == MA_BF16 ? kNsTileBf16 : kNsTileF32;
   std::vector<Range> ranges;
   for (int i = 0; i < n; ++i) {
     const ma_muon_tensor& x = t[i];
@@ -215,22 +258,23 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
 
   // Tile maps.
   const int T = P.gemm_tile;
-  std::vector<Item> ew, fin, sym, app, rows_nt, cols_t, rows_t, cols_nt, out;
+  std::vector<Item> ew, fin, gram, sq, app, rows_nt, cols_t, rows_t, cols_nt, out;
   int64_t tot_ew = 0, tot_sym = 0, tot_app = 0, tot_out = 0;
   for (int k = 0; k < nm; ++k) {
     const MatPlan& mp = P.mats[k];
-    const int nt = mp.rp / T;
+    const int nt = (mp.rp + T - 1) / T, ntc = (mp.cp + T - 1) / T;
     ew.push_back({k, mp.ntile_ew, 0});
     fin.push_back({k, 1, 0});
-    sym.push_back({k, nt * (nt + 1) / 2, static_cast<int64_t>(mp.cp) * 4 + mp.rp});  // Gram tile work ~ cp
-    app.push_back({k, nt * (mp.cp / T), mp.rp});
+    gram.push_back({k, nt * (nt + 1) / 2, mp.cp});  // per-tile work ~ contraction length
+    sq.push_back({k, nt * (nt + 1) / 2, mp.rp});
+    app.push_back({k, nt * ntc, mp.rp});
     const int rows_blocks = (mp.r + 3) / 4, col_blocks = (mp.c + 63) / 64;
     if (mp.tall) { cols_t.push_back({k, col_blocks, 0}); rows_t.push_back({k, rows_blocks, 0}); }
     else { rows_nt.push_back({k, rows_blocks, 0}); cols_nt.push_back({k, col_blocks, 0}); }
     out.push_back({k, ((mp.m + kEw - 1) / kEw) * ((mp.n + kEw - 1) / kEw), 0});
     tot_ew += mp.ntile_ew;
     tot_sym += nt * (nt + 1) / 2;
-    tot_app += static_cast<int64_t>(nt) * (mp.cp / T);
+    tot_app += static_cast<int64_t>(nt) * ntc;
     tot_out += static_cast<int64_t>((mp.m + kEw - 1) / kEw) * ((mp.n + kEw - 1) / kEw);
   }
   const int64_t kMaxGrid = (int64_t(1) << 31) - 1;
@@ -238,8 +282,10 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     return fail(MA_E_UNSUPPORTED, "step too large for one launch");
   P.ew = add_map(P, ew);
   P.fin_all = add_map(P, fin);
-  P.sym = add_map(P, sym);
-  P.app = add_map(P, app);
+  const bool xcd = hp->ns_dtype == MA_BF16;
+  P.gram = add_map(P, gram, xcd);
+  P.sq = add_map(P, sq, xcd);
+  P.app = add_map(P, app, xcd);
   P.rows_nt = add_map(P, rows_nt);
   P.cols_t = add_map(P, cols_t);
   P.rows_t = add_map(P, rows_t);
@@ -275,6 +321,12 @@ TileMap device_map(const MapRef& r, char* tables, size_t desc_bytes) {
   tm.perm = reinterpret_cast<const int32_t*>(tables + desc_bytes + r.perm_off);
   tm.nmat = r.nmat;
   tm.total = r.total;
+  tm.grid = r.grid;
+  tm.xcd = r.xcd;
+  for (int x = 0; x < 8; ++x) {
+    tm.xbase[x] = r.xbase[x];
+    tm.xcnt[x] = r.xcnt[x];
+  }
   return tm;
 }
 
@@ -415,7 +467,7 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
   const int bf = P.ns_dt == MA_BF16;
   for (int it = 0; it < hp->ns_steps; ++it) {
     for (int op = NS_GRAM; op <= NS_APPLY; ++op) {
-      const TileMap tm = TM(op == NS_APPLY ? P.app : P.sym);
+      const TileMap tm = TM(op == NS_APPLY ? P.app : (op == NS_GRAM ? P.gram : P.sq));
       timed(kNsNames[bf][op], s, [&] {
         if (bf)
           launch_ns_bf16(op, mats, tm, it & 1, it == 0, hp->ns_a, hp->ns_b, hp->ns_c, s);

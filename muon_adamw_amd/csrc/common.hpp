@@ -15,6 +15,11 @@ enum : int32_t { CAUT_NONE = 0, CAUT_WD_MASK = 1, CAUT_WRAPPER = 2 };
 constexpr int kPad = 128;
 // Element tile of the momentum pass, the reductions and the apply pass.
 constexpr int kEw = 64;
+// Output tile edge of the Newton-Schulz GEMMs (bf16 matrix-core / fp32 paths).
+// The bf16 tile may overhang a 128-padded matrix; its loads clamp and its
+// stores are masked.
+constexpr int kNsTileBf16 = 256;
+constexpr int kNsTileF32 = 64;
 
 // One matrix: one view of one batch entry of one Muon tensor, plus its
 // workspace buffers. Built on the host, read by every Muon kernel.
@@ -50,21 +55,37 @@ struct MatDesc {
 };
 
 // Maps a flat block index to (matrix, local tile) for one launch: matrices
-// are visited in `perm` order; entry k owns blocks [start[k], start[k+1]).
+// are visited in `perm` order; entry k owns tiles [start[k], start[k+1]).
+//
+// With `xcd` set the launch is XCD-aware: the hardware hands workgroup b to
+// XCD b % 8, so tile lists are laid out XCD-major (all tiles of a matrix on
+// one XCD, sharing its L2) and block b takes tile xbase[b % 8] + b / 8 of its
+// XCD's list, or exits if that list is shorter.
 struct TileMap {
   const int32_t* start;  // nmat + 1 prefix sums
   const int32_t* perm;   // nmat matrix indices
   int32_t nmat;
-  int32_t total;         // start[nmat]
+  int32_t total;         // tiles (= start[nmat])
+  int32_t grid;          // blocks to launch
+  int32_t xcd;           // 1: XCD-aware decode below
+  int32_t xbase[8];
+  int32_t xcnt[8];
 };
 
-__device__ __forceinline__ int find_entry(const TileMap& tm, int blk) {
+__device__ __forceinline__ int find_entry(const TileMap& tm, int tile) {
   int lo = 0, hi = tm.nmat - 1;
   while (lo < hi) {
     int mid = (lo + hi + 1) >> 1;
-    if (tm.start[mid] <= blk) lo = mid; else hi = mid - 1;
+    if (tm.start[mid] <= tile) lo = mid; else hi = mid - 1;
   }
   return lo;
+}
+
+// Block -> tile index of the launch, or -1 for an idle block.
+__device__ __forceinline__ int block_tile(const TileMap& tm, int blk) {
+  if (!tm.xcd) return blk;
+  const int x = blk & 7, s = blk >> 3;
+  return s < tm.xcnt[x] ? tm.xbase[x] + s : -1;
 }
 
 // bf16 <-> fp32. Stores round to nearest even (quiet NaN kept).

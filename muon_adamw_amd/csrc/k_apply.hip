@@ -97,10 +97,10 @@ void launch_apply(const MatDesc* mats, TileMap tm, int ns_dt, int src, int mode,
                   int use_cfac, hipStream_t s) {
   if (tm.total == 0) return;
   if (ns_dt == DT_BF16)
-    hipLaunchKernelGGL(apply_kernel<uint16_t>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, mode, cautious,
+    hipLaunchKernelGGL(apply_kernel<uint16_t>, dim3(tm.grid), dim3(256), 0, s, mats, tm, src, mode, cautious,
                        use_rfac, use_cfac);
   else
-    hipLaunchKernelGGL(apply_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, mode, cautious,
+    hipLaunchKernelGGL(apply_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, src, mode, cautious,
                        use_rfac, use_cfac);
 }
 

@@ -141,14 +141,14 @@ void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, flo
                      hipStream_t s) {
   if (tm.total == 0) return;
   if (ns_dt == DT_BF16)
-    hipLaunchKernelGGL(momentum_kernel<uint16_t>, dim3(tm.total), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
+    hipLaunchKernelGGL(momentum_kernel<uint16_t>, dim3(tm.grid), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
   else
-    hipLaunchKernelGGL(momentum_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
+    hipLaunchKernelGGL(momentum_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
 }
 
 void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, hipStream_t s) {
   if (tm.total == 0) return;
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(tm.total), dim3(256), 0, s, mats, tm, eps);
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(tm.grid), dim3(256), 0, s, mats, tm, eps);
 }
 
 }  // namespace ma

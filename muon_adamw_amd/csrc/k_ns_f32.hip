@@ -155,11 +155,11 @@ void launch_ns_f32(int op, const MatDesc* mats, TileMap tm, int src, int first, 
   if (tm.total == 0) return;
   NsArgs g{mats, tm, src, first, a, b, c};
   if (op == NS_GRAM)
-    hipLaunchKernelGGL(ns_f32_kernel<OP_GRAM>, dim3(tm.total), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ns_f32_kernel<OP_GRAM>, dim3(tm.grid), dim3(256), 0, s, g);
   else if (op == NS_SQUARE)
-    hipLaunchKernelGGL(ns_f32_kernel<OP_SQUARE>, dim3(tm.total), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ns_f32_kernel<OP_SQUARE>, dim3(tm.grid), dim3(256), 0, s, g);
   else
-    hipLaunchKernelGGL(ns_f32_kernel<OP_APPLY>, dim3(tm.total), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ns_f32_kernel<OP_APPLY>, dim3(tm.grid), dim3(256), 0, s, g);
 }
 
 }  // namespace ma

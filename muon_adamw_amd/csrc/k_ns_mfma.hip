@@ -9,18 +9,34 @@
 //                                     computed and each is stored twice
 //   SQUARE  B  = b A + c A A^T       A is symmetric, so A^2 = A A^T: the same
 //                                     row-by-row contraction; B is symmetric
-//   APPLY   X' = s1 * (a X + B X)    contraction over r with X read k-major
-// Storage is row-major bf16 everywhere; the first two are "NT" products (both
-// operands contiguous along the contraction), the third reads X transposed
-// into LDS.
+//   APPLY   X' = s1 * (a X + B X)    contraction over r, X read k-major
+// Storage is row-major bf16 everywhere.
 //
-// Tiles: 128 x 128 outputs per 256-thread block, four waves of 64 x 64, each
-// wave a 2 x 2 grid of v_mfma_f32_32x32x16_bf16. K advances 64 per stage
-// through a double-buffered LDS pipeline (global loads for stage k+1 are in
-// flight while stage k computes). The epilogue stages the fp32 accumulators
-// in LDS and writes 16-byte rows (and the mirrored tile for the symmetric
-// products), folding in the combine terms and the first iteration's
-// normalisation sigma = 1/(||Q||_F + eps).
+// Block: 256 x 256 outputs, 512 threads = 8 wave64s in a 2 x 4 grid, each
+// wave 128 x 64 outputs = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (128 fp32
+// accumulators per lane). The contraction advances 32 per stage. Both
+// operands go straight from HBM into LDS with global_load_lds_dwordx4 (no
+// staging registers), four stages deep (4 x 32 KB):
+//   * operands contiguous along the contraction (all of GRAM and SQUARE, B in
+//     APPLY) land as 64-byte rows, the four 16-byte chunks XOR-swizzled by row
+//     so that fragment reads of 8 or 16 consecutive rows hit distinct banks;
+//   * APPLY's X lands as it is stored (32 k-rows of 512 B), chunks swizzled
+//     by k, and its MFMA fragments are read with ds_read_b64_tr_b16: lane j of
+//     each 16-lane group addresses (k0 + j/4, n0 + 4 (j%4)) and lane i then
+//     holds k0..k0+3 of column n0 + i, the matrix-core operand layout.
+// The direct loads place the swizzle by choosing each lane's source chunk.
+// Waits are explicit: a plain s_barrier plus s_waitcnt vmcnt(8), the loads of
+// the two stages younger than the one about to be read (the tail re-loads
+// the last stage so the count stays constant). Workgroups are dealt to XCDs
+// so that all tiles of a matrix share one L2. Edge tiles (dimensions that are
+// multiples of 128 but not of 256) clamp their loads and mask their stores.
+//
+// Epilogue: the direct tile goes through LDS in four passes of 64 fp32 rows
+// and leaves as rows of 8-byte stores (one float4 of LDS per lane); the mirrored tile of the symmetric products
+// leaves straight from the accumulators, whose layout already gives each lane
+// four consecutive elements of a mirror row. The combine terms (b A + c A^2,
+// a X + B X) and the first iteration's normalisation sigma = 1/(||Q||_F + eps)
+// are applied in fp32 on the way out.
 #include "kernels.hpp"
 
 namespace ma {
@@ -28,14 +44,28 @@ namespace ma {
 namespace {
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef short i16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x16 __attribute__((ext_vector_type(16)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
+typedef __attribute__((address_space(1))) u32x4 g_u32x4_w;
+typedef __attribute__((address_space(1))) const u32x2 g_u32x2;
+typedef __attribute__((address_space(1))) u32x2 g_u32x2_w;
 
-constexpr int BM = 128;        // tile rows
-constexpr int BN = 128;        // tile cols
-constexpr int BK = 64;         // contraction per stage
-constexpr int LDA = BK + 8;    // LDS row pitch in bf16 (144 B: rows stay 16-B aligned, reads spread over banks)
-constexpr int OPS = BM * LDA;  // one operand stage
-constexpr int CP = BN + 4;     // fp32 epilogue pitch
+constexpr int BM = 256;
+constexpr int BN = 256;
+constexpr int BK = 32;
+constexpr int NTHR = 512;
+constexpr int RB = BK * 2;               // bytes per LDS row of a contraction-contiguous operand
+constexpr int XR = BN * 2;               // bytes per LDS row of APPLY's k-major X (512)
+constexpr int OPB = BM * RB;             // bytes per operand per stage (16 KB; X: 32 x 512)
+constexpr int NSTAGE = 4;                // direct-load pipeline depth
+constexpr int SMEM = NSTAGE * 2 * OPB;   // 128 KB
+constexpr int EPR = 64;                  // accumulator rows per epilogue pass
+constexpr int EPP = BN + 8;              // fp32 pitch of the staged rows
+static_assert(EPR * EPP * 4 <= SMEM, "epilogue staging must fit");
 
 enum { OP_GRAM = 0, OP_SQUARE = 1, OP_APPLY = 2 };
 
@@ -47,6 +77,48 @@ struct NsArgs {
   float a, b, c;
 };
 
+__device__ __forceinline__ u32x4 gload16(const uint16_t* p) { return *(g_u32x4*)(p); }
+__device__ __forceinline__ void gstore16(uint16_t* p, u32x4 v) { *(g_u32x4_w*)(p) = v; }
+__device__ __forceinline__ u32x2 gload8(const uint16_t* p) { return *(g_u32x2*)(p); }
+__device__ __forceinline__ void gstore8(uint16_t* p, u32x2 v) { *(g_u32x2_w*)(p) = v; }
+
+// 16 bytes per lane from global memory straight into LDS: lane l's data lands
+// at lds + 16 * l (lds must be the same for the whole wave).
+__device__ __forceinline__ void dma16(const uint16_t* g, char* lds) {
+  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
+                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+}
+#define MA_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
+
+// Transposing LDS read, issued as inline assembly so that the compiler adds
+// no wait for the in-flight direct loads (the builtin would get a full
+// vmcnt(0) in front of it). The caller waits with tr_wait() before use.
+template <int OFF>
+__device__ __forceinline__ i16x4 ds_read_tr(uint32_t lds_addr) {
+  i16x4 v;
+  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFF));
+  return v;
+}
+__device__ __forceinline__ void tr_wait(i16x4& a, i16x4& b, i16x4& c, i16x4& d) {
+  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
+}
+__device__ __forceinline__ uint32_t lds_addr(const char* p) {
+  return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
+}
+
+// Contraction-contiguous operand rows (64 B): the 16-byte chunks are XORed
+// with (row / 4) mod 4. A fragment read (32 consecutive rows, one chunk each
+// half-wave) then spreads every 16-lane quarter over all 16 bank groups of
+// the 256-byte bank line: measured conflict-free on gfx950, where the row
+// parity mixes of other swizzles cost 25% more cycles.
+__device__ __forceinline__ int swz(int row) { return (row >> 2) & 3; }
+__device__ __forceinline__ int lds_off(int row, int chunk) { return row * RB + ((chunk ^ swz(row)) << 4); }
+// APPLY's X rows (512 B, indexed by k): chunk XOR 4 (k mod 4), so the four
+// k-rows of one transposing read land in distinct 64-byte quarters of the
+// 256-byte bank line (measured conflict-free; unswizzled rows cost 1.5x).
+__device__ __forceinline__ int xswz(int k) { return (k & 3) << 2; }
+__device__ __forceinline__ int xoff(int k, int chunk) { return k * XR + ((chunk ^ xswz(k)) << 4); }
+
 __device__ __forceinline__ void tri_decode(int k, int& ti, int& tj) {
   int i = static_cast<int>((sqrtf(8.0f * k + 1.0f) - 1.0f) * 0.5f);
   while ((i + 1) * (i + 2) / 2 <= k) ++i;
@@ -54,72 +126,6 @@ __device__ __forceinline__ void tri_decode(int k, int& ti, int& tj) {
   ti = i;
   tj = k - i * (i + 1) / 2;
 }
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
-typedef __attribute__((address_space(1))) const u32x4 g_u32x4;
-
-// 16-byte load through a global-address-space pointer (a plain generic
-// pointer would become a flat load, which also counts against the LDS
-// counter and forces early waits).
-__device__ __forceinline__ u32x4 gload16(const uint16_t* p) { return *(g_u32x4*)(p); }
-
-// Operand staging registers for one 64-deep stage: four 16-byte chunks.
-struct Stage4 {
-  u32x4 v0, v1, v2, v3;
-};
-
-// 128 rows x 64 k of a row-major matrix, contraction contiguous.
-__device__ __forceinline__ Stage4 load_nt(const uint16_t* base, int ld, int k0) {
-  const int q = threadIdx.x, row = q >> 3, kc = (q & 7) * 8;
-  const uint16_t* p = base + (int64_t)row * ld + k0 + kc;
-  const int64_t step = (int64_t)32 * ld;   // 256 threads cover 32 rows per chunk
-  Stage4 r;
-  r.v0 = gload16(p);
-  r.v1 = gload16(p + step);
-  r.v2 = gload16(p + 2 * step);
-  r.v3 = gload16(p + 3 * step);
-  return r;
-}
-__device__ __forceinline__ void store_nt(uint16_t* sm, const Stage4& r) {
-  const int q = threadIdx.x, row = q >> 3, kc = (q & 7) * 8;
-  uint16_t* p = sm + row * LDA + kc;
-  *reinterpret_cast<u32x4*>(p) = r.v0;
-  *reinterpret_cast<u32x4*>(p + 32 * LDA) = r.v1;
-  *reinterpret_cast<u32x4*>(p + 64 * LDA) = r.v2;
-  *reinterpret_cast<u32x4*>(p + 96 * LDA) = r.v3;
-}
-// 64 k-rows x 128 columns of a row-major matrix (columns contiguous), to be
-// stored transposed (column-major in k) in LDS. Each thread owns 4 k-rows x 8
-// columns.
-__device__ __forceinline__ Stage4 load_nn(const uint16_t* base, int ld, int k0) {
-  const int kq = threadIdx.x & 15, nc = threadIdx.x >> 4;
-  const uint16_t* p = base + (int64_t)(k0 + kq * 4) * ld + nc * 8;
-  Stage4 r;
-  r.v0 = gload16(p);
-  r.v1 = gload16(p + ld);
-  r.v2 = gload16(p + 2 * ld);
-  r.v3 = gload16(p + 3 * ld);
-  return r;
-}
-__device__ __forceinline__ void store_nn(uint16_t* sm, const Stage4& r) {
-  const int kq = threadIdx.x & 15, nc = threadIdx.x >> 4;
-#pragma unroll
-  for (int w = 0; w < 4; ++w) {
-    const uint32_t a = r.v0[w], b = r.v1[w], c = r.v2[w], d = r.v3[w];
-    // columns 2w and 2w+1 of the four k-rows
-    u32x2 lo, hi;
-    lo.x = __builtin_amdgcn_perm(b, a, 0x05040100u);   // (a.lo, b.lo)
-    lo.y = __builtin_amdgcn_perm(d, c, 0x05040100u);   // (c.lo, d.lo)
-    hi.x = __builtin_amdgcn_perm(b, a, 0x07060302u);   // (a.hi, b.hi)
-    hi.y = __builtin_amdgcn_perm(d, c, 0x07060302u);   // (c.hi, d.hi)
-    *reinterpret_cast<u32x2*>(sm + (nc * 8 + 2 * w) * LDA + kq * 4) = lo;
-    *reinterpret_cast<u32x2*>(sm + (nc * 8 + 2 * w + 1) * LDA + kq * 4) = hi;
-  }
-}
-
-typedef __attribute__((address_space(1))) u32x4 g_u32x4_w;
-__device__ __forceinline__ void gstore16(uint16_t* p, u32x4 v) { *(g_u32x4_w*)(p) = v; }
 
 __device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
@@ -137,158 +143,264 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 }
 
 template <int OP>
-__global__ __launch_bounds__(256, 2) void ns_mfma_kernel(NsArgs args) {
-  __shared__ __attribute__((aligned(16))) uint16_t smem[2 * 2 * OPS];
+__global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
 
-  const int blk = blockIdx.x;
-  const int e = find_entry(args.tm, blk);
+  const int t_all = block_tile(args.tm, blockIdx.x);
+  if (t_all < 0) return;
+  const int e = find_entry(args.tm, t_all);
   const MatDesc& d = args.mats[args.tm.perm[e]];
-  const int t = blk - args.tm.start[e];
+  const int t = t_all - args.tm.start[e];
+  const int rp = d.rp, cp = d.cp;
   int ti, tj;
   if (OP == OP_APPLY) {
-    const int ntc = d.cp / BN;
+    const int ntc = (cp + BN - 1) / BN;
     ti = t / ntc;
     tj = t % ntc;
   } else {
     tri_decode(t, ti, tj);
   }
   const uint16_t* Xin = static_cast<const uint16_t*>(args.src ? d.x1 : d.x0);
-  const int rp = d.rp, cp = d.cp;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
-  const uint16_t* Aop;   // rows ti*BM.., contraction contiguous
-  const uint16_t* Bop;   // NT: rows tj*BN..; NN: columns tj*BN..
-  int lda, ldb, K;
+  // Operand geometry.
+  const uint16_t* Abase;
+  const uint16_t* Bbase;
+  int lda, ldb, K, limA, limB;
   if (OP == OP_GRAM) {
-    Aop = Xin + (int64_t)ti * BM * cp; Bop = Xin + (int64_t)tj * BN * cp; lda = ldb = cp; K = cp;
+    Abase = Xin; Bbase = Xin; lda = ldb = cp; K = cp; limA = limB = rp;
   } else if (OP == OP_SQUARE) {
-    const uint16_t* A = static_cast<const uint16_t*>(d.a);
-    Aop = A + (int64_t)ti * BM * rp; Bop = A + (int64_t)tj * BN * rp; lda = ldb = rp; K = rp;
+    Abase = Bbase = static_cast<const uint16_t*>(d.a); lda = ldb = rp; K = rp; limA = limB = rp;
   } else {
-    const uint16_t* B = static_cast<const uint16_t*>(d.b);
-    Aop = B + (int64_t)ti * BM * rp; lda = rp;
-    Bop = Xin + tj * BN; ldb = cp; K = rp;
+    Abase = static_cast<const uint16_t*>(d.b); lda = rp; limA = rp;
+    Bbase = Xin; ldb = cp; limB = cp; K = rp;
   }
+  const int nk = K / BK;
 
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6, wr = w >> 1, wc = w & 1;
-  f32x16 acc[2][2];
+  // Direct loads of a contraction-contiguous operand: wave w fills tile rows
+  // [32w, 32w+32) with two 16-row instructions; lane l takes LDS slot
+  // (row 16i + l/4, slot l%4) and loads the chunk the swizzle places there.
+  const int drow0 = 32 * w + (lane >> 2), drow1 = drow0 + 16;
+  const int dch0 = (lane & 3) ^ swz(drow0), dch1 = (lane & 3) ^ swz(drow1);
+  const uint16_t* ga0 = Abase + (int64_t)min(ti * BM + drow0, limA - 1) * lda + dch0 * 8;
+  const uint16_t* ga1 = Abase + (int64_t)min(ti * BM + drow1, limA - 1) * lda + dch1 * 8;
+  const uint16_t* gb0;
+  const uint16_t* gb1;
+  if (OP != OP_APPLY) {
+    gb0 = Bbase + (int64_t)min(tj * BN + drow0, limB - 1) * ldb + dch0 * 8;
+    gb1 = Bbase + (int64_t)min(tj * BN + drow1, limB - 1) * ldb + dch1 * 8;
+  } else {
+    // X: wave w fills k-rows 4w..4w+3, two rows (2 x 512 B) per instruction;
+    // lane l takes row 4w + 2i + l/32, slot l%32.
+    const int xr0 = 4 * w + (lane >> 5), xr1 = xr0 + 2;
+    const int xc0 = (lane & 31) ^ xswz(xr0), xc1 = (lane & 31) ^ xswz(xr1);
+    gb0 = Bbase + (int64_t)xr0 * ldb + min(tj * BN + xc0 * 8, limB - 8);
+    gb1 = Bbase + (int64_t)xr1 * ldb + min(tj * BN + xc1 * 8, limB - 8);
+  }
+  const int dlds = w * 32 * RB;   // == 4 * w * XR: the wave's first LDS byte in a stage
+  char* const Abuf = smem;                         // NSTAGE x OPB
+  char* const Bbuf = smem + NSTAGE * OPB;          // NSTAGE x OPB
+
+  auto issue = [&](int stage) {   // stage may run past nk: the last stage is re-read
+    const int ks = min(stage, nk - 1);
+    const int64_t koffA = (int64_t)ks * BK;
+    char* a = Abuf + (stage % NSTAGE) * OPB + dlds;
+    char* b = Bbuf + (stage % NSTAGE) * OPB + dlds;
+    dma16(ga0 + koffA, a);
+    dma16(ga1 + koffA, a + 16 * RB);
+    if (OP != OP_APPLY) {
+      dma16(gb0 + koffA, b);
+      dma16(gb1 + koffA, b + 16 * RB);
+    } else {
+      const int64_t koffX = (int64_t)ks * BK * ldb;
+      dma16(gb0 + koffX, b);
+      dma16(gb1 + koffX, b + 2 * XR);
+    }
+  };
+
+  const int wr = w >> 2, wc = w & 3, khalf = lane >> 5;
+  int arow[4];
 #pragma unroll
-  for (int i = 0; i < 2; ++i)
+  for (int i = 0; i < 4; ++i) arow[i] = wr * 128 + i * 32 + (lane & 31);
+  // B fragments: NT rows, or APPLY's transposing-read coordinates.
+  int brow[2];
+#pragma unroll
+  for (int j = 0; j < 2; ++j) brow[j] = wc * 64 + j * 32 + (lane & 31);
+  const int q16 = lane >> 4, i16 = lane & 15;
+  int xoff_base[2][2];   // [j][t] byte offset of the k-row/column a lane reads, k0 = 0
+#pragma unroll
+  for (int j = 0; j < 2; ++j)
+#pragma unroll
+    for (int tt = 0; tt < 2; ++tt) {
+      const int n = wc * 64 + j * 32 + 16 * (q16 & 1) + 4 * (i16 & 3);
+      const int k = 8 * (q16 >> 1) + 4 * tt + (i16 >> 2);
+      xoff_base[j][tt] = xoff(k, n >> 3) + (n & 7) * 2;
+    }
+
+  f32x16 acc[4][2];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  Stage4 ra = load_nt(Aop, lda, 0);
-  Stage4 rb = (OP == OP_APPLY) ? load_nn(Bop, ldb, 0) : load_nt(Bop, ldb, 0);
-  store_nt(smem, ra);
-  if (OP == OP_APPLY) store_nn(smem + OPS, rb); else store_nt(smem + OPS, rb);
-  __syncthreads();
-
-  const int nk = K / BK;
-  for (int kt = 0; kt < nk; ++kt) {
-    const int cur = kt & 1;
-    const bool more = kt + 1 < nk;
-    if (more) {
-      ra = load_nt(Aop, lda, (kt + 1) * BK);
-      rb = (OP == OP_APPLY) ? load_nn(Bop, ldb, (kt + 1) * BK) : load_nt(Bop, ldb, (kt + 1) * BK);
-    }
-    const uint16_t* As = smem + cur * 2 * OPS;
-    const uint16_t* Bs = As + OPS;
+  auto compute = [&](const char* As, const char* Bs) {
+    const uint32_t bx0 = (OP == OP_APPLY) ? lds_addr(Bs) + xoff_base[0][0] : 0;
+    const uint32_t bx1 = (OP == OP_APPLY) ? lds_addr(Bs) + xoff_base[1][0] : 0;
 #pragma unroll
     for (int ks = 0; ks < BK / 16; ++ks) {
-      bf16x8 af[2], bfv[2];
-      const int koff = ks * 16 + (lane >> 5) * 8;
+      const int ch = ks * 2 + khalf;
+      bf16x8 af[4], bfv[2];
+      if (OP == OP_APPLY) {
+        // k-rows advance by 16 per k-substep; the swizzle depends on k mod 4
+        // only, so the offsets shift by whole rows. xoff_base[j][1] is
+        // xoff_base[j][0] + 4 rows.
+        i16x4 l0, h0, l1, h1;
+        if (ks == 0) {
+          l0 = ds_read_tr<0>(bx0);
+          h0 = ds_read_tr<4 * XR>(bx0);
+          l1 = ds_read_tr<0>(bx1);
+          h1 = ds_read_tr<4 * XR>(bx1);
+        } else {
+          l0 = ds_read_tr<16 * XR>(bx0);
+          h0 = ds_read_tr<20 * XR>(bx0);
+          l1 = ds_read_tr<16 * XR>(bx1);
+          h1 = ds_read_tr<20 * XR>(bx1);
+        }
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        af[i] = *reinterpret_cast<const bf16x8*>(As + (wr * 64 + i * 32 + (lane & 31)) * LDA + koff);
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(arow[i], ch));
+        tr_wait(l0, h0, l1, h1);
+        const short __attribute__((ext_vector_type(8))) b0 = {l0[0], l0[1], l0[2], l0[3], h0[0], h0[1], h0[2], h0[3]};
+        const short __attribute__((ext_vector_type(8))) b1 = {l1[0], l1[1], l1[2], l1[3], h1[0], h1[1], h1[2], h1[3]};
+        bfv[0] = __builtin_bit_cast(bf16x8, b0);
+        bfv[1] = __builtin_bit_cast(bf16x8, b1);
+      } else {
 #pragma unroll
-      for (int j = 0; j < 2; ++j)
-        bfv[j] = *reinterpret_cast<const bf16x8*>(Bs + (wc * 64 + j * 32 + (lane & 31)) * LDA + koff);
+        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(arow[i], ch));
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
+        for (int j = 0; j < 2; ++j) bfv[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(brow[j], ch));
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
         for (int j = 0; j < 2; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
     }
-    if (more) {
-      uint16_t* nxt = smem + (cur ^ 1) * 2 * OPS;
-      store_nt(nxt, ra);
-      if (OP == OP_APPLY) store_nn(nxt + OPS, rb); else store_nt(nxt + OPS, rb);
-    }
-    __syncthreads();
-  }
+  };
 
-  // Epilogue: accumulators -> LDS (fp32), then 16-byte rows out.
-  float* Cs = reinterpret_cast<float*>(smem);
-#pragma unroll
-  for (int i = 0; i < 2; ++i)
-#pragma unroll
-    for (int j = 0; j < 2; ++j)
-#pragma unroll
-      for (int v = 0; v < 16; ++v) {
-        const int row = wr * 64 + i * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-        const int col = wc * 64 + j * 32 + (lane & 31);
-        Cs[row * CP + col] = acc[i][j][v];
-      }
+  // Each stage's direct loads are 4 instructions per wave, so when stage kt
+  // is read the 8 loads of stages kt+1 and kt+2 may still be in flight.
+  issue(0);
+  issue(1);
+  issue(2);
+  for (int kt = 0; kt < nk; ++kt) {
+    MA_WAIT_VM(8);
+    __builtin_amdgcn_s_barrier();
+    issue(kt + 3);   // into the buffer read during iteration kt-1
+    compute(Abuf + (kt % NSTAGE) * OPB, Bbuf + (kt % NSTAGE) * OPB);
+  }
+  // drain the trailing re-loads before the epilogue reuses LDS
+  MA_WAIT_VM(0);
   __syncthreads();
 
+  // ---------------------------------------------------------------- epilogue
   float alpha = 1.f;
   if (args.first) {
     const float sg = d.stat[0];
     alpha = (OP == OP_GRAM) ? sg * sg : (OP == OP_APPLY ? sg : 1.f);
   }
   uint16_t* out;
-  int ldo;
+  int ldo, limR, limC;
   const uint16_t* extra = nullptr;
-  if (OP == OP_GRAM) { out = static_cast<uint16_t*>(d.a); ldo = rp; }
-  else if (OP == OP_SQUARE) { out = static_cast<uint16_t*>(d.b); ldo = rp; extra = static_cast<const uint16_t*>(d.a); }
-  else { out = static_cast<uint16_t*>(args.src ? d.x0 : d.x1); ldo = cp; extra = Xin; }
-
-#pragma unroll 2
-  for (int p = 0; p < 8; ++p) {
-    const int q = threadIdx.x + 256 * p, row = q >> 4, cc = (q & 15) * 8;
-    float v[8];
-    const float4 c0 = *reinterpret_cast<const float4*>(Cs + row * CP + cc);
-    const float4 c1 = *reinterpret_cast<const float4*>(Cs + row * CP + cc + 4);
-    v[0] = c0.x; v[1] = c0.y; v[2] = c0.z; v[3] = c0.w;
-    v[4] = c1.x; v[5] = c1.y; v[6] = c1.z; v[7] = c1.w;
-    const int64_t go = (int64_t)(ti * BM + row) * ldo + tj * BN + cc;
-    if (OP == OP_GRAM) {
-#pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] *= alpha;
-    } else {
-      float x[8];
-      unpack8(gload16(extra + go), x);
-      if (OP == OP_SQUARE) {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = args.b * x[u] + args.c * v[u];
-      } else {
-#pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = alpha * (args.a * x[u] + v[u]);
-      }
-    }
-    gstore16(out + go, pack8(v));
+  if (OP == OP_GRAM) {
+    out = static_cast<uint16_t*>(d.a); ldo = rp; limR = rp; limC = rp;
+  } else if (OP == OP_SQUARE) {
+    out = static_cast<uint16_t*>(d.b); ldo = rp; limR = rp; limC = rp; extra = static_cast<const uint16_t*>(d.a);
+  } else {
+    out = static_cast<uint16_t*>(args.src ? d.x0 : d.x1); ldo = cp; limR = rp; limC = cp; extra = Xin;
   }
+
   if (OP != OP_APPLY && ti != tj) {
-    // mirrored tile (tj, ti): element (r', c') = C(c', r')
-#pragma unroll 2
-    for (int p = 0; p < 8; ++p) {
-      const int q = threadIdx.x + 256 * p, row = q >> 4, cc = (q & 15) * 8;
-      float v[8];
+    // mirrored tile (tj, ti) straight from the accumulators: lane holds rows
+    // r0..r0+3 of tile column c, i.e. four consecutive entries of mirror row c
 #pragma unroll
-      for (int u = 0; u < 8; ++u) v[u] = Cs[(cc + u) * CP + row];
-      const int64_t go = (int64_t)(tj * BN + row) * ldo + ti * BM + cc;
-      if (OP == OP_GRAM) {
+    for (int i = 0; i < 4; ++i)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] *= alpha;
-      } else {
-        float x[8];
-        unpack8(gload16(extra + go), x);
+      for (int j = 0; j < 2; ++j)
 #pragma unroll
-        for (int u = 0; u < 8; ++u) v[u] = args.b * x[u] + args.c * v[u];
+        for (int g = 0; g < 4; ++g) {
+          const int c = wc * 64 + j * 32 + (lane & 31);
+          const int r0 = wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+          const int gr = tj * BN + c, gc = ti * BM + r0;
+          if (gr < limR && gc < limC) {
+            const int64_t go = (int64_t)gr * ldo + gc;
+            float v[4];
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = acc[i][j][4 * g + u];
+            if (OP == OP_GRAM) {
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] *= alpha;
+            } else {
+              const u32x2 xx = gload8(extra + go);
+              const float x[4] = {__uint_as_float(xx.x << 16), __uint_as_float(xx.x & 0xffff0000u),
+                                  __uint_as_float(xx.y << 16), __uint_as_float(xx.y & 0xffff0000u)};
+#pragma unroll
+              for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
+            }
+            u32x2 o;
+            o.x = pack_bf16x2(v[0], v[1]);
+            o.y = pack_bf16x2(v[2], v[3]);
+            gstore8(out + go, o);
+          }
+        }
+  }
+
+  float* Cs = reinterpret_cast<float*>(smem);
+#pragma unroll
+  for (int p = 0; p < 4; ++p) {
+    // staged row sr = wr*32 + r  <->  tile row wr*128 + p*32 + r
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int v = 0; v < 16; ++v) {
+        const int sr = wr * 32 + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+        const int col = wc * 64 + j * 32 + (lane & 31);
+        Cs[sr * EPP + col] = acc[p][j][v];
       }
-      gstore16(out + go, pack8(v));
+    __syncthreads();
+#pragma unroll
+    for (int it = 0; it < (EPR * BN / 4) / NTHR; ++it) {
+      // one float4 per lane: consecutive lanes read consecutive 16 bytes
+      const int q = tid + NTHR * it, sr = q >> 6, cc = (q & 63) * 4;
+      const int gr = ti * BM + (sr >> 5) * 128 + p * 32 + (sr & 31);
+      const int gc = tj * BN + cc;
+      if (gr < limR && gc < limC) {
+        const f32x4 c4 = *reinterpret_cast<const f32x4*>(Cs + sr * EPP + cc);
+        float v[4] = {c4.x, c4.y, c4.z, c4.w};
+        const int64_t go = (int64_t)gr * ldo + gc;
+        if (OP == OP_GRAM) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] *= alpha;
+        } else {
+          const u32x2 xx = gload8(extra + go);
+          const float x[4] = {__uint_as_float(xx.x << 16), __uint_as_float(xx.x & 0xffff0000u),
+                              __uint_as_float(xx.y << 16), __uint_as_float(xx.y & 0xffff0000u)};
+          if (OP == OP_SQUARE) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
+          } else {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = alpha * (args.a * x[u] + v[u]);
+          }
+        }
+        u32x2 o;
+        o.x = pack_bf16x2(v[0], v[1]);
+        o.y = pack_bf16x2(v[2], v[3]);
+        gstore8(out + go, o);
+      }
     }
+    __syncthreads();
   }
 }
 
@@ -299,11 +411,11 @@ void launch_ns_bf16(int op, const MatDesc* mats, TileMap tm, int src, int first,
   if (tm.total == 0) return;
   NsArgs g{mats, tm, src, first, a, b, c};
   if (op == NS_GRAM)
-    hipLaunchKernelGGL(ns_mfma_kernel<OP_GRAM>, dim3(tm.total), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ns_mfma_kernel<OP_GRAM>, dim3(tm.grid), dim3(NTHR), 0, s, g);
   else if (op == NS_SQUARE)
-    hipLaunchKernelGGL(ns_mfma_kernel<OP_SQUARE>, dim3(tm.total), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ns_mfma_kernel<OP_SQUARE>, dim3(tm.grid), dim3(NTHR), 0, s, g);
   else
-    hipLaunchKernelGGL(ns_mfma_kernel<OP_APPLY>, dim3(tm.total), dim3(256), 0, s, g);
+    hipLaunchKernelGGL(ns_mfma_kernel<OP_APPLY>, dim3(tm.grid), dim3(NTHR), 0, s, g);
 }
 
 }  // namespace ma

@@ -139,27 +139,27 @@ __global__ __launch_bounds__(256) void finalize_muon_plus_kernel(const MatDesc* 
 void launch_canon_rowsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, int weighted, hipStream_t s) {
   if (tm.total == 0) return;
   if (ns_dt == DT_BF16)
-    hipLaunchKernelGGL(canon_rowsum_kernel<uint16_t>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, weighted);
+    hipLaunchKernelGGL(canon_rowsum_kernel<uint16_t>, dim3(tm.grid), dim3(256), 0, s, mats, tm, src, weighted);
   else
-    hipLaunchKernelGGL(canon_rowsum_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, weighted);
+    hipLaunchKernelGGL(canon_rowsum_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, src, weighted);
 }
 
 void launch_canon_colsum(const MatDesc* mats, TileMap tm, int ns_dt, int src, int weighted, hipStream_t s) {
   if (tm.total == 0) return;
   if (ns_dt == DT_BF16)
-    hipLaunchKernelGGL(canon_colsum_kernel<uint16_t>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, weighted);
+    hipLaunchKernelGGL(canon_colsum_kernel<uint16_t>, dim3(tm.grid), dim3(256), 0, s, mats, tm, src, weighted);
   else
-    hipLaunchKernelGGL(canon_colsum_kernel<float>, dim3(tm.total), dim3(256), 0, s, mats, tm, src, weighted);
+    hipLaunchKernelGGL(canon_colsum_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, src, weighted);
 }
 
 void launch_finalize_normuon(const MatDesc* mats, TileMap tm, float one_minus_beta2, hipStream_t s) {
   if (tm.total == 0) return;
-  hipLaunchKernelGGL(finalize_normuon_kernel, dim3(tm.total), dim3(256), 0, s, mats, tm, one_minus_beta2);
+  hipLaunchKernelGGL(finalize_normuon_kernel, dim3(tm.grid), dim3(256), 0, s, mats, tm, one_minus_beta2);
 }
 
 void launch_finalize_muon_plus(const MatDesc* mats, TileMap tm, int stage, float eps, hipStream_t s) {
   if (tm.total == 0) return;
-  hipLaunchKernelGGL(finalize_muon_plus_kernel, dim3(tm.total), dim3(256), 0, s, mats, tm, stage, eps);
+  hipLaunchKernelGGL(finalize_muon_plus_kernel, dim3(tm.grid), dim3(256), 0, s, mats, tm, stage, eps);
 }
 
 }  // namespace ma
