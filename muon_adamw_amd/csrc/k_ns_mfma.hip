@@ -16,7 +16,7 @@
 // wave 128 x 64 outputs = 4 x 2 tiles of v_mfma_f32_32x32x16_bf16 (128 fp32
 // accumulators per lane). The contraction advances 32 per stage. Both
 // operands go straight from HBM into LDS with global_load_lds_dwordx4 (no
-// staging registers), four stages deep (4 x 32 KB):
+// staging registers), four stages deep (4 x 32 KB).
 //   * operands contiguous along the contraction (all of GRAM and SQUARE, B in
 //     APPLY) land as 64-byte rows, the four 16-byte chunks XOR-swizzled by row
 //     so that fragment reads of 8 or 16 consecutive rows hit distinct banks;
@@ -25,10 +25,13 @@
 //     each 16-lane group addresses (k0 + j/4, n0 + 4 (j%4)) and lane i then
 //     holds k0..k0+3 of column n0 + i, the matrix-core operand layout.
 // The direct loads place the swizzle by choosing each lane's source chunk.
-// Waits are explicit: a plain s_barrier plus s_waitcnt vmcnt(8), the loads of
-// the two stages younger than the one about to be read (the tail re-loads
-// the last stage so the count stays constant). Workgroups are dealt to XCDs
-// so that all tiles of a matrix share one L2. Edge tiles (dimensions that are
+// Each stage is split into two k-substeps of 16 whose fragments are double
+// buffered in registers, so the LDS reads of one substep overlap the matrix
+// multiplies of the other. All waits are explicit (s_waitcnt in inline
+// assembly, a plain s_barrier): the compiler would otherwise wait for all
+// memory traffic at every barrier and LDS read. The tail re-loads the last
+// stage so the wait counts stay constant. Workgroups are dealt to XCDs so
+// that all tiles of a matrix share one L2. Edge tiles (dimensions that are
 // multiples of 128 but not of 256) clamp their loads and mask their stores.
 //
 // Epilogue: the direct tile goes through LDS in four passes of 64 fp32 rows
@@ -37,6 +40,8 @@
 // four consecutive elements of a mirror row. The combine terms (b A + c A^2,
 // a X + B X) and the first iteration's normalisation sigma = 1/(||Q||_F + eps)
 // are applied in fp32 on the way out.
+#include <type_traits>
+
 #include "kernels.hpp"
 
 namespace ma {
@@ -83,25 +88,21 @@ __device__ __forceinline__ u32x2 gload8(const uint16_t* p) { return *(g_u32x2*)(
 __device__ __forceinline__ void gstore8(uint16_t* p, u32x2 v) { *(g_u32x2_w*)(p) = v; }
 
 // 16 bytes per lane from global memory straight into LDS: lane l's data lands
-// at lds + 16 * l (lds must be the same for the whole wave).
-__device__ __forceinline__ void dma16(const uint16_t* g, char* lds) {
-  __builtin_amdgcn_global_load_lds((__attribute__((address_space(1))) void*)(g),
-                                   (__attribute__((address_space(3))) void*)(lds), 16, 0, 0);
+// at lds + 16 * l (lds is the wave's LDS byte address, uniform). Issued as
+// inline assembly so that the compiler does not see a load into LDS: it would
+// then wait for every such load (vmcnt(0)) in front of LDS reads it cannot
+// prove disjoint. The hardware counts these loads in vmcnt only, never in
+// lgkmcnt, so the compiler's own waits for LDS reads stay exact; the waits
+// for the loads themselves are explicit (MA_WAIT_VM). M0 holds the LDS
+// address; one wait state (the s_nop) separates its write from the load.
+__device__ __forceinline__ void dma16(const uint16_t* g, uint32_t lds) {
+  asm volatile("s_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+               :
+               : "v"(g), "{m0}"(__builtin_amdgcn_readfirstlane(lds))
+               : "memory");
 }
 #define MA_WAIT_VM(n) asm volatile("s_waitcnt vmcnt(" #n ")" ::: "memory")
 
-// Transposing LDS read, issued as inline assembly so that the compiler adds
-// no wait for the in-flight direct loads (the builtin would get a full
-// vmcnt(0) in front of it). The caller waits with tr_wait() before use.
-template <int OFF>
-__device__ __forceinline__ i16x4 ds_read_tr(uint32_t lds_addr) {
-  i16x4 v;
-  asm volatile("ds_read_b64_tr_b16 %0, %1 offset:%2" : "=v"(v) : "v"(lds_addr), "i"(OFF));
-  return v;
-}
-__device__ __forceinline__ void tr_wait(i16x4& a, i16x4& b, i16x4& c, i16x4& d) {
-  asm volatile("s_waitcnt lgkmcnt(0)" : "+v"(a), "+v"(b), "+v"(c), "+v"(d));
-}
 __device__ __forceinline__ uint32_t lds_addr(const char* p) {
   return static_cast<uint32_t>(reinterpret_cast<uintptr_t>((__attribute__((address_space(3))) const char*)p));
 }
@@ -200,12 +201,15 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   const int dlds = w * 32 * RB;   // == 4 * w * XR: the wave's first LDS byte in a stage
   char* const Abuf = smem;                         // NSTAGE x OPB
   char* const Bbuf = smem + NSTAGE * OPB;          // NSTAGE x OPB
+  const uint32_t a_lds = lds_addr(Abuf) + dlds, b_lds = lds_addr(Bbuf) + dlds;
 
-  auto issue = [&](int stage) {   // stage may run past nk: the last stage is re-read
+  // Direct loads of stage `stage` into LDS buffer `buf` (4 instructions per
+  // wave). Stages past the end re-load the last one, so the wait counts below
+  // stay constant.
+  auto issue = [&](int stage, int buf) {
     const int ks = min(stage, nk - 1);
     const int64_t koffA = (int64_t)ks * BK;
-    char* a = Abuf + (stage % NSTAGE) * OPB + dlds;
-    char* b = Bbuf + (stage % NSTAGE) * OPB + dlds;
+    const uint32_t a = a_lds + buf * OPB, b = b_lds + buf * OPB;
     dma16(ga0 + koffA, a);
     dma16(ga1 + koffA, a + 16 * RB);
     if (OP != OP_APPLY) {
@@ -219,23 +223,28 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   };
 
   const int wr = w >> 2, wc = w & 3, khalf = lane >> 5;
-  int arow[4];
+  // Per-lane LDS offsets of the fragments, [k-substep]: A rows, NT B rows.
+  int aoff[4][2], boff[2][2];
 #pragma unroll
-  for (int i = 0; i < 4; ++i) arow[i] = wr * 128 + i * 32 + (lane & 31);
-  // B fragments: NT rows, or APPLY's transposing-read coordinates.
-  int brow[2];
+  for (int q = 0; q < 2; ++q) {
 #pragma unroll
-  for (int j = 0; j < 2; ++j) brow[j] = wc * 64 + j * 32 + (lane & 31);
-  const int q16 = lane >> 4, i16 = lane & 15;
-  int xoff_base[2][2];   // [j][t] byte offset of the k-row/column a lane reads, k0 = 0
+    for (int i = 0; i < 4; ++i) aoff[i][q] = lds_off(wr * 128 + i * 32 + (lane & 31), q * 2 + khalf);
 #pragma unroll
-  for (int j = 0; j < 2; ++j)
+    for (int j = 0; j < 2; ++j) boff[j][q] = lds_off(wc * 64 + j * 32 + (lane & 31), q * 2 + khalf);
+  }
+  // APPLY's X fragments: offset of the k-row/column a lane's transposing read
+  // starts at (k0 = 0); the other reads of a stage are whole-row shifts of
+  // it, because the swizzle depends on k mod 4 only.
+  int xoffs[2] = {0, 0};
+  if (OP == OP_APPLY) {
+    const int q16 = lane >> 4, i16 = lane & 15;
 #pragma unroll
-    for (int tt = 0; tt < 2; ++tt) {
+    for (int j = 0; j < 2; ++j) {
       const int n = wc * 64 + j * 32 + 16 * (q16 & 1) + 4 * (i16 & 3);
-      const int k = 8 * (q16 >> 1) + 4 * tt + (i16 >> 2);
-      xoff_base[j][tt] = xoff(k, n >> 3) + (n & 7) * 2;
+      const int k = 8 * (q16 >> 1) + (i16 >> 2);
+      xoffs[j] = xoff(k, n >> 3) + (n & 7) * 2;
     }
+  }
 
   f32x16 acc[4][2];
 #pragma unroll
@@ -245,60 +254,84 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
 #pragma unroll
       for (int v = 0; v < 16; ++v) acc[i][j][v] = 0.f;
 
-  auto compute = [&](const char* As, const char* Bs) {
-    const uint32_t bx0 = (OP == OP_APPLY) ? lds_addr(Bs) + xoff_base[0][0] : 0;
-    const uint32_t bx1 = (OP == OP_APPLY) ? lds_addr(Bs) + xoff_base[1][0] : 0;
+  // Fragment double buffer: while the matrix cores work through one
+  // k-substep the LDS reads of the next are in flight (the compiler places
+  // the LDS waits; scheduling barriers keep each read batch ahead of the
+  // multiplies it overlaps).
+  struct Frag {
+    bf16x8 a[4];
+    bf16x8 b[2];
+  };
+  Frag F0, F1;
+
+  auto read = [&](Frag& f, int soff, auto Q_) {   // soff: byte offset of the stage's buffer
+    constexpr int Q = decltype(Q_)::value;
+    const char* As = Abuf + soff;
+    const char* Bs = Bbuf + soff;
+    if constexpr (OP == OP_APPLY) {
 #pragma unroll
-    for (int ks = 0; ks < BK / 16; ++ks) {
-      const int ch = ks * 2 + khalf;
-      bf16x8 af[4], bfv[2];
-      if (OP == OP_APPLY) {
-        // k-rows advance by 16 per k-substep; the swizzle depends on k mod 4
-        // only, so the offsets shift by whole rows. xoff_base[j][1] is
-        // xoff_base[j][0] + 4 rows.
-        i16x4 l0, h0, l1, h1;
-        if (ks == 0) {
-          l0 = ds_read_tr<0>(bx0);
-          h0 = ds_read_tr<4 * XR>(bx0);
-          l1 = ds_read_tr<0>(bx1);
-          h1 = ds_read_tr<4 * XR>(bx1);
-        } else {
-          l0 = ds_read_tr<16 * XR>(bx0);
-          h0 = ds_read_tr<20 * XR>(bx0);
-          l1 = ds_read_tr<16 * XR>(bx1);
-          h1 = ds_read_tr<20 * XR>(bx1);
-        }
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(arow[i], ch));
-        tr_wait(l0, h0, l1, h1);
-        const short __attribute__((ext_vector_type(8))) b0 = {l0[0], l0[1], l0[2], l0[3], h0[0], h0[1], h0[2], h0[3]};
-        const short __attribute__((ext_vector_type(8))) b1 = {l1[0], l1[1], l1[2], l1[3], h1[0], h1[1], h1[2], h1[3]};
-        bfv[0] = __builtin_bit_cast(bf16x8, b0);
-        bfv[1] = __builtin_bit_cast(bf16x8, b1);
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) af[i] = *reinterpret_cast<const bf16x8*>(As + lds_off(arow[i], ch));
-#pragma unroll
-        for (int j = 0; j < 2; ++j) bfv[j] = *reinterpret_cast<const bf16x8*>(Bs + lds_off(brow[j], ch));
+      for (int j = 0; j < 2; ++j) {
+        const char* p = Bs + xoffs[j] + Q * 16 * XR;
+        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(p));
+        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
+            (__attribute__((address_space(3))) i16x4*)(p + 4 * XR));
+        const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3],
+                                                             hi[0], hi[1], hi[2], hi[3]};
+        f.b[j] = __builtin_bit_cast(bf16x8, v);
       }
+    } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 2; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[i], bfv[j], acc[i][j], 0, 0, 0);
+      for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + boff[j][Q]);
     }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(As + aoff[i][Q]);
+  };
+  auto mma = [&](const Frag& f) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(f.a[i], f.b[j], acc[i][j], 0, 0, 0);
+  };
+  using I0 = std::integral_constant<int, 0>;
+  using I1 = std::integral_constant<int, 1>;
+
+  // One stage kt (LDS buffer S = kt mod 4), entered with F0 = (kt, substep
+  // 0) in flight: read (kt, 1) into F1 and multiply F0; then wait for stage
+  // kt+1 (own loads, then the barrier for everybody's), refill the buffer
+  // read in stage kt-1 with stage kt+3, read (kt+1, 0) into F0 and multiply
+  // F1. Every wave's reads of stage kt-1 completed before its last multiply
+  // of that stage, so the refill after the barrier overwrites nothing live.
+  // The buffer index is a compile-time constant (the loop is unrolled by
+  // four), so LDS offsets fold into the instructions.
+  auto stage = [&](int kt, auto S_) {
+    constexpr int S = decltype(S_)::value;
+    read(F1, S * OPB, I1{});
+    __builtin_amdgcn_sched_barrier(0);   // keep the reads ahead of the multiplies
+    mma(F0);
+    __builtin_amdgcn_sched_barrier(0);
+    MA_WAIT_VM(4);
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_sched_barrier(0);
+    issue(kt + 3, (S + 3) % NSTAGE);
+    read(F0, ((S + 1) % NSTAGE) * OPB, I0{});
+    __builtin_amdgcn_sched_barrier(0);
+    mma(F1);
+    __builtin_amdgcn_sched_barrier(0);
   };
 
-  // Each stage's direct loads are 4 instructions per wave, so when stage kt
-  // is read the 8 loads of stages kt+1 and kt+2 may still be in flight.
-  issue(0);
-  issue(1);
-  issue(2);
-  for (int kt = 0; kt < nk; ++kt) {
-    MA_WAIT_VM(8);
-    __builtin_amdgcn_s_barrier();
-    issue(kt + 3);   // into the buffer read during iteration kt-1
-    compute(Abuf + (kt % NSTAGE) * OPB, Bbuf + (kt % NSTAGE) * OPB);
+  issue(0, 0);
+  issue(1, 1);
+  issue(2, 2);
+  MA_WAIT_VM(8);
+  __builtin_amdgcn_s_barrier();
+  read(F0, 0, I0{});
+  for (int kt = 0; kt < nk; kt += NSTAGE) {   // nk is a multiple of 4
+    stage(kt, std::integral_constant<int, 0>{});
+    stage(kt + 1, std::integral_constant<int, 1>{});
+    stage(kt + 2, std::integral_constant<int, 2>{});
+    stage(kt + 3, std::integral_constant<int, 3>{});
   }
   // drain the trailing re-loads before the epilogue reuses LDS
   MA_WAIT_VM(0);
