@@ -354,44 +354,80 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
     out = static_cast<uint16_t*>(args.src ? d.x0 : d.x1); ldo = cp; limR = rp; limC = cp; extra = Xin;
   }
 
+  // Every load of the combine term reads a clamped, always valid address, so
+  // a batch of them issues back to back; only the stores are predicated
+  // (edge tiles of a 128-padded matrix). Extents are multiples of 4, so the
+  // four elements of a store are all in or all out.
+  auto unpack4 = [](u32x2 xx, float* x) {
+    x[0] = __uint_as_float(xx.x << 16); x[1] = __uint_as_float(xx.x & 0xffff0000u);
+    x[2] = __uint_as_float(xx.y << 16); x[3] = __uint_as_float(xx.y & 0xffff0000u);
+  };
+  auto store4 = [&](int64_t go, const float* v) {
+    u32x2 o;
+    o.x = pack_bf16x2(v[0], v[1]);
+    o.y = pack_bf16x2(v[2], v[3]);
+    gstore8(out + go, o);
+  };
+
   if (OP != OP_APPLY && ti != tj) {
     // mirrored tile (tj, ti) straight from the accumulators: lane holds rows
     // r0..r0+3 of tile column c, i.e. four consecutive entries of mirror row c
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < 4; ++i) {
+      u32x2 xx[2][4];
+      int64_t go[2][4];
+      bool ok[2][4];
 #pragma unroll
       for (int j = 0; j < 2; ++j)
 #pragma unroll
         for (int g = 0; g < 4; ++g) {
-          const int c = wc * 64 + j * 32 + (lane & 31);
-          const int r0 = wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
-          const int gr = tj * BN + c, gc = ti * BM + r0;
-          if (gr < limR && gc < limC) {
-            const int64_t go = (int64_t)gr * ldo + gc;
-            float v[4];
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = acc[i][j][4 * g + u];
-            if (OP == OP_GRAM) {
-#pragma unroll
-              for (int u = 0; u < 4; ++u) v[u] *= alpha;
-            } else {
-              const u32x2 xx = gload8(extra + go);
-              const float x[4] = {__uint_as_float(xx.x << 16), __uint_as_float(xx.x & 0xffff0000u),
-                                  __uint_as_float(xx.y << 16), __uint_as_float(xx.y & 0xffff0000u)};
-#pragma unroll
-              for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
-            }
-            u32x2 o;
-            o.x = pack_bf16x2(v[0], v[1]);
-            o.y = pack_bf16x2(v[2], v[3]);
-            gstore8(out + go, o);
-          }
+          const int gr = tj * BN + wc * 64 + j * 32 + (lane & 31);
+          const int gc = ti * BM + wr * 128 + i * 32 + 8 * g + 4 * (lane >> 5);
+          ok[j][g] = gr < limR && gc < limC;
+          go[j][g] = (int64_t)min(gr, limR - 1) * ldo + min(gc, limC - 4);
+          if (OP == OP_SQUARE) xx[j][g] = gload8(extra + go[j][g]);
         }
+#pragma unroll
+      for (int j = 0; j < 2; ++j)
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          float v[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = acc[i][j][4 * g + u];
+          if (OP == OP_GRAM) {
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] *= alpha;
+          } else {
+            float x[4];
+            unpack4(xx[j][g], x);
+#pragma unroll
+            for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
+          }
+          if (ok[j][g]) store4(go[j][g], v);
+        }
+    }
   }
 
+  // Direct tile through LDS, 64 accumulator rows per pass; the pass's
+  // combine-term loads are issued before the staging so their latency
+  // overlaps it.
   float* Cs = reinterpret_cast<float*>(smem);
+  constexpr int PER = (EPR * BN / 4) / NTHR;   // float4 groups per lane and pass
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
+    u32x2 xx[PER];
+    int64_t go[PER];
+    bool ok[PER];
+#pragma unroll
+    for (int it = 0; it < PER; ++it) {
+      // one float4 per lane: consecutive lanes read consecutive 16 bytes
+      const int q = tid + NTHR * it, sr = q >> 6, cc = (q & 63) * 4;
+      const int gr = ti * BM + (sr >> 5) * 128 + p * 32 + (sr & 31);
+      const int gc = tj * BN + cc;
+      ok[it] = gr < limR && gc < limC;
+      go[it] = (int64_t)min(gr, limR - 1) * ldo + min(gc, limC - 4);
+      if (OP != OP_GRAM) xx[it] = gload8(extra + go[it]);
+    }
     // staged row sr = wr*32 + r  <->  tile row wr*128 + p*32 + r
 #pragma unroll
     for (int j = 0; j < 2; ++j)
@@ -403,35 +439,25 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
       }
     __syncthreads();
 #pragma unroll
-    for (int it = 0; it < (EPR * BN / 4) / NTHR; ++it) {
-      // one float4 per lane: consecutive lanes read consecutive 16 bytes
+    for (int it = 0; it < PER; ++it) {
       const int q = tid + NTHR * it, sr = q >> 6, cc = (q & 63) * 4;
-      const int gr = ti * BM + (sr >> 5) * 128 + p * 32 + (sr & 31);
-      const int gc = tj * BN + cc;
-      if (gr < limR && gc < limC) {
-        const f32x4 c4 = *reinterpret_cast<const f32x4*>(Cs + sr * EPP + cc);
-        float v[4] = {c4.x, c4.y, c4.z, c4.w};
-        const int64_t go = (int64_t)gr * ldo + gc;
-        if (OP == OP_GRAM) {
+      const f32x4 c4 = *reinterpret_cast<const f32x4*>(Cs + sr * EPP + cc);
+      float v[4] = {c4.x, c4.y, c4.z, c4.w};
+      if (OP == OP_GRAM) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] *= alpha;
+        for (int u = 0; u < 4; ++u) v[u] *= alpha;
+      } else {
+        float x[4];
+        unpack4(xx[it], x);
+        if (OP == OP_SQUARE) {
+#pragma unroll
+          for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
         } else {
-          const u32x2 xx = gload8(extra + go);
-          const float x[4] = {__uint_as_float(xx.x << 16), __uint_as_float(xx.x & 0xffff0000u),
-                              __uint_as_float(xx.y << 16), __uint_as_float(xx.y & 0xffff0000u)};
-          if (OP == OP_SQUARE) {
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
-          } else {
-#pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = alpha * (args.a * x[u] + v[u]);
-          }
+          for (int u = 0; u < 4; ++u) v[u] = alpha * (args.a * x[u] + v[u]);
         }
-        u32x2 o;
-        o.x = pack_bf16x2(v[0], v[1]);
-        o.y = pack_bf16x2(v[2], v[3]);
-        gstore8(out + go, o);
       }
+      if (ok[it]) store4(go[it], v);
     }
     __syncthreads();
   }
