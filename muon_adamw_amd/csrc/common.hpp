@@ -102,13 +102,25 @@ __device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
   return __builtin_bit_cast(uint32_t, h);
 }
 
+// Global-memory view of a generic pointer (one read from a descriptor, say):
+// accesses through it compile to global_* instructions instead of FLAT ones,
+// which also count in lgkmcnt and cost more to issue.
+// (clang vector types: HIP's float4 and friends are classes whose members
+// cannot be used through an address-space-qualified pointer)
+typedef float gf4 __attribute__((ext_vector_type(4)));
+typedef uint32_t gu2 __attribute__((ext_vector_type(2)));
+template <typename T>
+__device__ __forceinline__ __attribute__((address_space(1))) T* gmem(T* p) {
+  return (__attribute__((address_space(1))) T*)(p);
+}
+
 __device__ __forceinline__ float load_elem(const void* p, int64_t i, int dt) {
-  return dt == DT_BF16 ? bf16_to_f32(static_cast<const uint16_t*>(p)[i])
-                       : static_cast<const float*>(p)[i];
+  return dt == DT_BF16 ? bf16_to_f32(gmem(static_cast<const uint16_t*>(p))[i])
+                       : gmem(static_cast<const float*>(p))[i];
 }
 __device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float v) {
-  if (dt == DT_BF16) static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
-  else static_cast<float*>(p)[i] = v;
+  if (dt == DT_BF16) gmem(static_cast<uint16_t*>(p))[i] = f32_to_bf16(v);
+  else gmem(static_cast<float*>(p))[i] = v;
 }
 
 // Wave64 sum in a fixed butterfly order (deterministic).

@@ -19,14 +19,34 @@ template <typename XT>
 __device__ __forceinline__ void load4(const XT* p, float* v);
 template <>
 __device__ __forceinline__ void load4<float>(const float* p, float* v) {
-  const float4 x = *reinterpret_cast<const float4*>(p);
+  const gf4 x = *gmem(reinterpret_cast<const gf4*>(p));
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
 }
 template <>
 __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
-  const uint2 x = *reinterpret_cast<const uint2*>(p);
+  const gu2 x = *gmem(reinterpret_cast<const gu2*>(p));
   v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
   v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
+}
+
+// Four consecutive stored elements (the caller guarantees 16-byte alignment
+// for fp32 and 8-byte alignment for bf16 via the descriptor's vec flag).
+__device__ __forceinline__ void load4v(const void* p, int64_t i, int dt, float* v) {
+  if (dt == DT_BF16) {
+    load4<uint16_t>(static_cast<const uint16_t*>(p) + i, v);
+  } else {
+    load4<float>(static_cast<const float*>(p) + i, v);
+  }
+}
+__device__ __forceinline__ void store4v(void* p, int64_t i, int dt, const float* v) {
+  if (dt == DT_BF16) {
+    gu2 x;
+    x.x = pack_bf16x2(v[0], v[1]);
+    x.y = pack_bf16x2(v[2], v[3]);
+    *gmem(reinterpret_cast<gu2*>(static_cast<uint16_t*>(p) + i)) = x;
+  } else {
+    *gmem(reinterpret_cast<gf4*>(static_cast<float*>(p) + i)) = gf4{v[0], v[1], v[2], v[3]};
+  }
 }
 
 template <typename XT>
@@ -61,32 +81,73 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
   for (int p = 0; p < 4; ++p) {
     const int lr = tr + 16 * p, si = s0 + lr;
     if (si >= m) continue;
-    const float rf = use_rfac ? d.rfac[si] : 1.f;
+    const float rf = use_rfac ? gmem(d.rfac)[si] : 1.f;
+    const int sj0 = c0 + tc;
+    if (sj0 >= n) continue;
+    float uu[4];
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
-      const int sj = c0 + tc + u;
-      if (sj >= n) continue;
-      float uu = d.tall ? us[tc + u][lr] : us[lr][tc + u];
-      if (use_rfac) uu *= rf;
-      if (use_cfac) uu *= d.cfac[sj];
-      const int64_t idx = (int64_t)si * n + sj;
+      uu[u] = d.tall ? us[tc + u][lr] : us[lr][tc + u];
+      if (use_rfac) uu[u] *= rf;
+    }
+    const int64_t idx = (int64_t)si * n + sj0;
+    if (d.vec && sj0 + 3 < n) {
+      // four consecutive elements of the stored row: one 16-byte (fp32) or
+      // 8-byte (bf16) access per operand
+      if (use_cfac) {
+        const gf4 cf = *gmem(reinterpret_cast<const gf4*>(d.cfac + sj0));
+        uu[0] *= cf.x; uu[1] *= cf.y; uu[2] *= cf.z; uu[3] *= cf.w;
+      }
+      float w[4], wn[4];
+      if (mode != APPLY_COPY) load4v(d.param, idx, d.pdt, w);
       if (mode == APPLY_COPY) {
-        store_elem(d.param, idx, d.pdt, uu);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wn[u] = uu[u];
+      } else if (cautious == CAUT_NONE) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wn[u] = d.decay * w[u] - d.step * uu[u];
+      } else if (cautious == CAUT_WD_MASK) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wn[u] = w[u] - d.step * uu[u];
+          if (uu[u] * w[u] >= 0.f) wn[u] -= d.lrwd * w[u];
+        }
+      } else {
+        float g[4];
+        load4v(d.grad, idx, d.gdt, g);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float delta = d.lrwd * w[u] + d.step * uu[u];
+          wn[u] = (delta * g[u] > 0.f) ? w[u] - delta : w[u];
+        }
+      }
+      store4v(d.param, idx, d.pdt, wn);
+      continue;
+    }
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+      const int sj = sj0 + u;
+      if (sj >= n) continue;
+      float uv = uu[u];
+      if (use_cfac) uv *= gmem(d.cfac)[sj];
+      const int64_t ix = idx + u;
+      if (mode == APPLY_COPY) {
+        store_elem(d.param, ix, d.pdt, uv);
         continue;
       }
-      const float w = load_elem(d.param, idx, d.pdt);
+      const float w = load_elem(d.param, ix, d.pdt);
       float wn;
       if (cautious == CAUT_NONE) {
-        wn = d.decay * w - d.step * uu;
+        wn = d.decay * w - d.step * uv;
       } else if (cautious == CAUT_WD_MASK) {
-        wn = w - d.step * uu;
-        if (uu * w >= 0.f) wn -= d.lrwd * w;
+        wn = w - d.step * uv;
+        if (uv * w >= 0.f) wn -= d.lrwd * w;
       } else {
-        const float g = load_elem(d.grad, idx, d.gdt);
-        const float delta = d.lrwd * w + d.step * uu;
+        const float g = load_elem(d.grad, ix, d.gdt);
+        const float delta = d.lrwd * w + d.step * uv;
         wn = (delta * g > 0.f) ? w - delta : w;
       }
-      store_elem(d.param, idx, d.pdt, wn);
+      store_elem(d.param, ix, d.pdt, wn);
     }
   }
 }

@@ -20,14 +20,14 @@ __device__ __forceinline__ void store4(XT* dst, const float* v);
 
 template <>
 __device__ __forceinline__ void store4<float>(float* dst, const float* v) {
-  *reinterpret_cast<float4*>(dst) = make_float4(v[0], v[1], v[2], v[3]);
+  *gmem(reinterpret_cast<gf4*>(dst)) = gf4{v[0], v[1], v[2], v[3]};
 }
 template <>
 __device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, const float* v) {
-  uint2 p;
+  gu2 p;
   p.x = pack_bf16x2(v[0], v[1]);
   p.y = pack_bf16x2(v[2], v[3]);
-  *reinterpret_cast<uint2*>(dst) = p;
+  *gmem(reinterpret_cast<gu2*>(dst)) = p;
 }
 
 __device__ __forceinline__ float block_sum_256(float v, float* red) {
@@ -65,22 +65,22 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
       float g[4];
       if (d.vec && sc + 3 < n) {
         if (d.gdt == DT_BF16) {
-          const uint2 raw = *reinterpret_cast<const uint2*>(static_cast<const uint16_t*>(d.grad) + idx);
+          const gu2 raw = *gmem(reinterpret_cast<const gu2*>(static_cast<const uint16_t*>(d.grad) + idx));
           g[0] = __uint_as_float(raw.x << 16); g[1] = __uint_as_float(raw.x & 0xffff0000u);
           g[2] = __uint_as_float(raw.y << 16); g[3] = __uint_as_float(raw.y & 0xffff0000u);
         } else {
-          const float4 raw = *reinterpret_cast<const float4*>(static_cast<const float*>(d.grad) + idx);
+          const gf4 raw = *gmem(reinterpret_cast<const gf4*>(static_cast<const float*>(d.grad) + idx));
           g[0] = raw.x; g[1] = raw.y; g[2] = raw.z; g[3] = raw.w;
         }
         if (d.mom) {
-          float4 bm = *reinterpret_cast<const float4*>(d.mom + idx);
+          gf4 bm = *gmem(reinterpret_cast<const gf4*>(d.mom + idx));
           float b[4] = {bm.x, bm.y, bm.z, bm.w};
 #pragma unroll
           for (int u = 0; u < 4; ++u) {
             b[u] = beta * b[u] + omb * g[u];
             q[u] = nesterov ? g[u] + beta * (b[u] - g[u]) : b[u];
           }
-          *reinterpret_cast<float4*>(d.mom + idx) = make_float4(b[0], b[1], b[2], b[3]);
+          *gmem(reinterpret_cast<gf4*>(d.mom + idx)) = gf4{b[0], b[1], b[2], b[3]};
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) q[u] = g[u];
@@ -91,9 +91,9 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
           if (sc + u < n) {
             const float gu = load_elem(d.grad, idx + u, d.gdt);
             if (d.mom) {
-              float b = d.mom[idx + u];
+              float b = gmem(d.mom)[idx + u];
               b = beta * b + omb * gu;
-              d.mom[idx + u] = b;
+              gmem(d.mom)[idx + u] = b;
               q[u] = nesterov ? gu + beta * (b - gu) : b;
             } else {
               q[u] = gu;
@@ -122,7 +122,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
     store4<XT>(X + (int64_t)(i0 + ci) * d.cp + j0 + tc, v);
   }
   const float tot = block_sum_256(ss, red);
-  if (threadIdx.x == 0) d.part[t] = tot;
+  if (threadIdx.x == 0) gmem(d.part)[t] = tot;
 }
 
 __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ mats, TileMap tm,
@@ -130,9 +130,9 @@ __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __res
   __shared__ float red[4];
   const MatDesc& d = mats[tm.perm[blockIdx.x]];
   float s = 0.f;
-  for (int i = threadIdx.x; i < d.ntile_ew; i += 256) s += d.part[i];
+  for (int i = threadIdx.x; i < d.ntile_ew; i += 256) s += gmem(d.part)[i];
   const float tot = block_sum_256(s, red);
-  if (threadIdx.x == 0) d.stat[0] = 1.0f / (sqrtf(tot) + eps);
+  if (threadIdx.x == 0) gmem(d.stat)[0] = 1.0f / (sqrtf(tot) + eps);
 }
 
 }  // namespace

@@ -77,13 +77,13 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(NsArgs args) {
   const int lrow = threadIdx.x >> 2, lk = (threadIdx.x & 3) * 4;  // NT loads: 64 rows x 16 k
   const int nk = threadIdx.x >> 4, nc = (threadIdx.x & 15) * 4;   // NN loads: 16 k x 64 cols
   for (int k0 = 0; k0 < K; k0 += TK) {
-    const float4 va = *reinterpret_cast<const float4*>(Aop + (int64_t)lrow * lda + k0 + lk);
+    const gf4 va = *gmem(reinterpret_cast<const gf4*>(Aop + (int64_t)lrow * lda + k0 + lk));
     As[lk + 0][lrow] = va.x; As[lk + 1][lrow] = va.y; As[lk + 2][lrow] = va.z; As[lk + 3][lrow] = va.w;
     if (OP == OP_APPLY) {
-      const float4 vb = *reinterpret_cast<const float4*>(Bop + (int64_t)(k0 + nk) * ldb + nc);
-      *reinterpret_cast<float4*>(&Bs[nk][nc]) = vb;
+      const gf4 vb = *gmem(reinterpret_cast<const gf4*>(Bop + (int64_t)(k0 + nk) * ldb + nc));
+      *reinterpret_cast<gf4*>(&Bs[nk][nc]) = vb;
     } else {
-      const float4 vb = *reinterpret_cast<const float4*>(Bop + (int64_t)lrow * ldb + k0 + lk);
+      const gf4 vb = *gmem(reinterpret_cast<const gf4*>(Bop + (int64_t)lrow * ldb + k0 + lk));
       Bs[lk + 0][lrow] = vb.x; Bs[lk + 1][lrow] = vb.y; Bs[lk + 2][lrow] = vb.z; Bs[lk + 3][lrow] = vb.w;
     }
     __syncthreads();
@@ -103,7 +103,7 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(NsArgs args) {
 
   float alpha = 1.f;
   if (args.first) {
-    const float sg = d.stat[0];
+    const float sg = gmem(d.stat)[0];
     alpha = (OP == OP_GRAM) ? sg * sg : (OP == OP_APPLY ? sg : 1.f);
   }
   float* out;
@@ -121,13 +121,13 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(NsArgs args) {
 #pragma unroll
       for (int j = 0; j < 4; ++j) v[j] *= alpha;
     } else {
-      const float4 x = *reinterpret_cast<const float4*>(extra + go);
+      const gf4 x = *gmem(reinterpret_cast<const gf4*>(extra + go));
       const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
       for (int j = 0; j < 4; ++j)
         v[j] = (OP == OP_SQUARE) ? args.b * xv[j] + args.c * v[j] : alpha * (args.a * xv[j] + v[j]);
     }
-    *reinterpret_cast<float4*>(out + go) = make_float4(v[0], v[1], v[2], v[3]);
+    *gmem(reinterpret_cast<gf4*>(out + go)) = gf4{v[0], v[1], v[2], v[3]};
   }
   if (OP != OP_APPLY && ti != tj) {
 #pragma unroll
@@ -138,12 +138,12 @@ __global__ __launch_bounds__(256) void ns_f32_kernel(NsArgs args) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] *= alpha;
       } else {
-        const float4 x = *reinterpret_cast<const float4*>(extra + go);
+        const gf4 x = *gmem(reinterpret_cast<const gf4*>(extra + go));
         const float xv[4] = {x.x, x.y, x.z, x.w};
 #pragma unroll
         for (int i = 0; i < 4; ++i) v[i] = args.b * xv[i] + args.c * v[i];
       }
-      *reinterpret_cast<float4*>(out + go) = make_float4(v[0], v[1], v[2], v[3]);
+      *gmem(reinterpret_cast<gf4*>(out + go)) = gf4{v[0], v[1], v[2], v[3]};
     }
   }
 }

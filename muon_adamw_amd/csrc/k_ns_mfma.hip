@@ -340,7 +340,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   // ---------------------------------------------------------------- epilogue
   float alpha = 1.f;
   if (args.first) {
-    const float sg = d.stat[0];
+    const float sg = gmem(d.stat)[0];
     alpha = (OP == OP_GRAM) ? sg * sg : (OP == OP_APPLY ? sg : 1.f);
   }
   uint16_t* out;

@@ -36,7 +36,7 @@ __global__ __launch_bounds__(256) void canon_rowsum_kernel(const MatDesc* __rest
   if (weighted) {
     for (int j = lane; j < d.c; j += 64) {
       const float u = ld_x<XT>(U, j);
-      const float f = d.rfac[j];
+      const float f = gmem(d.rfac)[j];
       s += (u * u) * (f * f);
     }
   } else {
@@ -46,7 +46,7 @@ __global__ __launch_bounds__(256) void canon_rowsum_kernel(const MatDesc* __rest
     }
   }
   s = wave_sum(s);
-  if (lane == 0) d.csum_r[row] = s;
+  if (lane == 0) gmem(d.csum_r)[row] = s;
 }
 
 // 64 canonical columns per block: 16 row groups x 16 column quads; partials
@@ -63,7 +63,7 @@ __global__ __launch_bounds__(256) void canon_colsum_kernel(const MatDesc* __rest
   const XT* U = static_cast<const XT*>(src ? d.x1 : d.x0);
   float s[4] = {0.f, 0.f, 0.f, 0.f};
   for (int i = g; i < d.r; i += 16) {
-    const float w = weighted ? d.rfac[i] * d.rfac[i] : 1.f;
+    const float w = weighted ? gmem(d.rfac)[i] * gmem(d.rfac)[i] : 1.f;
     const int64_t base = (int64_t)i * d.cp + c0 + cq;
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
@@ -79,7 +79,7 @@ __global__ __launch_bounds__(256) void canon_colsum_kernel(const MatDesc* __rest
 #pragma unroll
     for (int k = 0; k < 16; ++k) t += part[k][threadIdx.x];
     const int col = c0 + threadIdx.x;
-    if (col < d.c) d.csum_c[col] = t;
+    if (col < d.c) gmem(d.csum_c)[col] = t;
   }
 }
 
@@ -105,11 +105,11 @@ __global__ __launch_bounds__(256) void finalize_normuon_kernel(const MatDesc* __
   float tot = 0.f, toth = 0.f;
   for (int i = threadIdx.x; i < d.m; i += 256) {
     const float s = rs[i];
-    float v = d.row_v[i];
+    float v = gmem(d.row_v)[i];
     v = v + omb2 * (s * inv_n - v);
-    d.row_v[i] = v;
+    gmem(d.row_v)[i] = v;
     const float di = 1.0f / sqrtf(fmaxf(v, 1e-30f));
-    d.rfac[i] = di;
+    gmem(d.rfac)[i] = di;
     tot += s;
     toth += s * (di * di);
   }
@@ -117,7 +117,7 @@ __global__ __launch_bounds__(256) void finalize_normuon_kernel(const MatDesc* __
   toth = block_sum_256(toth, red);
   const float kappa = sqrtf(tot) / fmaxf(sqrtf(toth), 1e-30f);
   __syncthreads();
-  for (int i = threadIdx.x; i < d.m; i += 256) d.rfac[i] *= kappa;
+  for (int i = threadIdx.x; i < d.m; i += 256) gmem(d.rfac)[i] *= kappa;
 }
 
 // Muon+: stage 1 rfac_i = 1/sqrt(stored row sum + eps); stage 2
@@ -127,10 +127,10 @@ __global__ __launch_bounds__(256) void finalize_muon_plus_kernel(const MatDesc* 
   const MatDesc& d = mats[tm.perm[blockIdx.x]];
   if (stage == 1) {
     const float* rs = d.tall ? d.csum_c : d.csum_r;
-    for (int i = threadIdx.x; i < d.m; i += 256) d.rfac[i] = 1.0f / sqrtf(rs[i] + eps);
+    for (int i = threadIdx.x; i < d.m; i += 256) gmem(d.rfac)[i] = 1.0f / sqrtf(rs[i] + eps);
   } else {
     const float* cs = d.tall ? d.csum_r : d.csum_c;
-    for (int j = threadIdx.x; j < d.n; j += 256) d.cfac[j] = 1.0f / sqrtf(cs[j] + eps);
+    for (int j = threadIdx.x; j < d.n; j += 256) gmem(d.cfac)[j] = 1.0f / sqrtf(cs[j] + eps);
   }
 }
 
