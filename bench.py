@@ -208,8 +208,13 @@ def main():
     ns_kernel_s = sum(prof[n][1] for n in prof if n.startswith("ns_")) / args.profile_steps / 1e3
     dominant = max(prof, key=lambda n: prof[n][1])
     dk = kernels[dominant]
+    # HBM bytes per launch from the committed counter summary of this
+    # workload (FETCH_SIZE/WRITE_SIZE passes, copy-calibrated), while the
+    # kernel sources are unchanged since it was taken
+    from muon_adamw_amd import counters
+    traffic = counters.traffic_for(os.path.join(HERE, "profiles", f"counters_{wl.name}.json"), dominant)
     roofline = {"bound": dk.get("bound"), "achieved": dk.get("achieved"), "peak": dk.get("peak"),
-                "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": None, "kernel": dominant}
+                "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": traffic, "kernel": dominant}
     muon_s = muon_ms / 1e3
     value = ns_total_flops / muon_s / 1e12
     line = {

@@ -79,28 +79,19 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
 
 // Lays out a launch's tile list. Plain maps keep one list ordered by
 // decreasing per-tile work (the dispatcher then runs longest tiles first).
-// XCD-aware maps first deal whole matrices to the 8 XCDs, longest total work
-// first onto the least-loaded XCD, then order each XCD's list the same way.
-MapRef add_map(Plan& P, std::vector<Item> items, bool xcd_aware = false) {
+// XCD-aware maps deal whole matrices to the 8 XCDs by `xcd_of` (the same
+// for all three Newton-Schulz launches, so a matrix's operands stay behind
+// one L2), then order each XCD's list by decreasing per-tile work.
+MapRef add_map(Plan& P, std::vector<Item> items, const std::vector<int>* xcd_of = nullptr) {
+  const bool xcd_aware = xcd_of != nullptr;
   auto by_key = [](const Item& x, const Item& y) { return x.key > y.key; };
   std::stable_sort(items.begin(), items.end(), by_key);
   MapRef r;
   r.nmat = static_cast<int>(items.size());
   std::vector<Item> order;
   if (xcd_aware && !items.empty()) {
-    std::vector<Item> byw = items;
-    std::stable_sort(byw.begin(), byw.end(), [](const Item& x, const Item& y) {
-      return x.key * x.tiles > y.key * y.tiles;
-    });
     std::vector<std::vector<Item>> bin(kXcds);
-    int64_t load[kXcds] = {0, 0, 0, 0, 0, 0, 0, 0};
-    for (const Item& it : byw) {
-      int b = 0;
-      for (int x = 1; x < kXcds; ++x)
-        if (load[x] < load[b]) b = x;
-      bin[b].push_back(it);
-      load[b] += it.key * it.tiles;
-    }
+    for (const Item& it : items) bin[(*xcd_of)[it.mat]].push_back(it);
     int64_t base = 0, maxc = 0;
     for (int x = 0; x < kXcds; ++x) {
       std::stable_sort(bin[x].begin(), bin[x].end(), by_key);
@@ -282,10 +273,31 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     return fail(MA_E_UNSUPPORTED, "step too large for one launch");
   P.ew = add_map(P, ew);
   P.fin_all = add_map(P, fin);
-  const bool xcd = hp->ns_dtype == MA_BF16;
-  P.gram = add_map(P, gram, xcd);
-  P.sq = add_map(P, sq, xcd);
-  P.app = add_map(P, app, xcd);
+  if (hp->ns_dtype == MA_BF16) {
+    // One XCD per matrix for all three GEMMs: longest total work first onto
+    // the least-loaded XCD.
+    std::vector<int64_t> work(nm);
+    for (int k = 0; k < nm; ++k)
+      work[k] = gram[k].key * gram[k].tiles + sq[k].key * sq[k].tiles + app[k].key * app[k].tiles;
+    std::vector<int> order(nm), xcd_of(nm, 0);
+    for (int k = 0; k < nm; ++k) order[k] = k;
+    std::stable_sort(order.begin(), order.end(), [&](int a, int b) { return work[a] > work[b]; });
+    int64_t load[kXcds] = {0, 0, 0, 0, 0, 0, 0, 0};
+    for (int k : order) {
+      int b = 0;
+      for (int x = 1; x < kXcds; ++x)
+        if (load[x] < load[b]) b = x;
+      xcd_of[k] = b;
+      load[b] += work[k];
+    }
+    P.gram = add_map(P, gram, &xcd_of);
+    P.sq = add_map(P, sq, &xcd_of);
+    P.app = add_map(P, app, &xcd_of);
+  } else {
+    P.gram = add_map(P, gram);
+    P.sq = add_map(P, sq);
+    P.app = add_map(P, app);
+  }
   P.rows_nt = add_map(P, rows_nt);
   P.cols_t = add_map(P, cols_t);
   P.rows_t = add_map(P, rows_t);

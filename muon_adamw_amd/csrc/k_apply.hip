@@ -63,6 +63,20 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
   const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
   const XT* U = static_cast<const XT*>(src ? d.x1 : d.x0);
 
+  // A full, aligned stored tile (the common case) issues its parameter (and
+  // gradient) loads first, so they are in flight together with the loads of
+  // U; edge tiles take the element-wise path below.
+  const bool full = d.vec && s0 + kEw <= m && c0 + kEw <= n;
+  float w[4][4], g[4][4];
+  if (full && mode != APPLY_COPY) {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int64_t idx = (int64_t)(s0 + tr + 16 * p) * n + c0 + tc;
+      load4v(d.param, idx, d.pdt, w[p]);
+      if (cautious == CAUT_WRAPPER) load4v(d.grad, idx, d.gdt, g[p]);
+    }
+  }
+
   // canonical tile covering this stored tile; the padded canonical buffer is
   // at least as large as the stored extent rounded up to 64, so all reads are
   // in bounds.
@@ -76,6 +90,44 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
     for (int u = 0; u < 4; ++u) us[lr][tc + u] = v[u];
   }
   __syncthreads();
+
+  if (full) {
+    float cf[4] = {1.f, 1.f, 1.f, 1.f};
+    if (use_cfac) {
+      const gf4 c4 = *gmem(reinterpret_cast<const gf4*>(d.cfac + c0 + tc));
+      cf[0] = c4.x; cf[1] = c4.y; cf[2] = c4.z; cf[3] = c4.w;
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int lr = tr + 16 * p;
+      const int64_t idx = (int64_t)(s0 + lr) * n + c0 + tc;
+      const float rf = use_rfac ? gmem(d.rfac)[s0 + lr] : 1.f;
+      float uu[4], wn[4];
+#pragma unroll
+      for (int u = 0; u < 4; ++u) uu[u] = (d.tall ? us[tc + u][lr] : us[lr][tc + u]) * rf * cf[u];
+      if (mode == APPLY_COPY) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wn[u] = uu[u];
+      } else if (cautious == CAUT_NONE) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) wn[u] = d.decay * w[p][u] - d.step * uu[u];
+      } else if (cautious == CAUT_WD_MASK) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          wn[u] = w[p][u] - d.step * uu[u];
+          if (uu[u] * w[p][u] >= 0.f) wn[u] -= d.lrwd * w[p][u];
+        }
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          const float delta = d.lrwd * w[p][u] + d.step * uu[u];
+          wn[u] = (delta * g[p][u] > 0.f) ? w[p][u] - delta : w[p][u];
+        }
+      }
+      store4v(d.param, idx, d.pdt, wn);
+    }
+    return;
+  }
 
 #pragma unroll
   for (int p = 0; p < 4; ++p) {

@@ -55,37 +55,53 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
   const int tr = threadIdx.x >> 4, tc = (threadIdx.x & 15) * 4;
   const int m = d.m, n = d.n;
 
-  // Phase 1: stored tile, coalesced along stored rows.
+  // Phase 1: stored tile, coalesced along stored rows. A full, aligned tile
+  // (the common case) issues all of a thread's loads before any use, so
+  // they are in flight together; edge tiles take the element-wise path.
+  const bool full = d.vec && sr0 + kEw <= m && sc0 + kEw <= n;
+  if (full) {
+    float g[4][4];
+    gf4 bm[4];
 #pragma unroll
-  for (int p = 0; p < 4; ++p) {
-    const int lr = tr + 16 * p, sr = sr0 + lr, sc = sc0 + tc;
-    float q[4] = {0.f, 0.f, 0.f, 0.f};
-    if (sr < m && sc < n) {
-      const int64_t idx = (int64_t)sr * n + sc;
-      float g[4];
-      if (d.vec && sc + 3 < n) {
-        if (d.gdt == DT_BF16) {
-          const gu2 raw = *gmem(reinterpret_cast<const gu2*>(static_cast<const uint16_t*>(d.grad) + idx));
-          g[0] = __uint_as_float(raw.x << 16); g[1] = __uint_as_float(raw.x & 0xffff0000u);
-          g[2] = __uint_as_float(raw.y << 16); g[3] = __uint_as_float(raw.y & 0xffff0000u);
-        } else {
-          const gf4 raw = *gmem(reinterpret_cast<const gf4*>(static_cast<const float*>(d.grad) + idx));
-          g[0] = raw.x; g[1] = raw.y; g[2] = raw.z; g[3] = raw.w;
-        }
-        if (d.mom) {
-          gf4 bm = *gmem(reinterpret_cast<const gf4*>(d.mom + idx));
-          float b[4] = {bm.x, bm.y, bm.z, bm.w};
-#pragma unroll
-          for (int u = 0; u < 4; ++u) {
-            b[u] = beta * b[u] + omb * g[u];
-            q[u] = nesterov ? g[u] + beta * (b[u] - g[u]) : b[u];
-          }
-          *gmem(reinterpret_cast<gf4*>(d.mom + idx)) = gf4{b[0], b[1], b[2], b[3]};
-        } else {
-#pragma unroll
-          for (int u = 0; u < 4; ++u) q[u] = g[u];
-        }
+    for (int p = 0; p < 4; ++p) {
+      const int64_t idx = (int64_t)(sr0 + tr + 16 * p) * n + sc0 + tc;
+      if (d.gdt == DT_BF16) {
+        const gu2 raw = *gmem(reinterpret_cast<const gu2*>(static_cast<const uint16_t*>(d.grad) + idx));
+        g[p][0] = __uint_as_float(raw.x << 16); g[p][1] = __uint_as_float(raw.x & 0xffff0000u);
+        g[p][2] = __uint_as_float(raw.y << 16); g[p][3] = __uint_as_float(raw.y & 0xffff0000u);
       } else {
+        const gf4 raw = *gmem(reinterpret_cast<const gf4*>(static_cast<const float*>(d.grad) + idx));
+        g[p][0] = raw.x; g[p][1] = raw.y; g[p][2] = raw.z; g[p][3] = raw.w;
+      }
+      if (d.mom) bm[p] = *gmem(reinterpret_cast<const gf4*>(d.mom + idx));
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int lr = tr + 16 * p;
+      const int64_t idx = (int64_t)(sr0 + lr) * n + sc0 + tc;
+      float q[4];
+      if (d.mom) {
+        float b[4] = {bm[p].x, bm[p].y, bm[p].z, bm[p].w};
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+          b[u] = beta * b[u] + omb * g[p][u];
+          q[u] = nesterov ? g[p][u] + beta * (b[u] - g[p][u]) : b[u];
+        }
+        *gmem(reinterpret_cast<gf4*>(d.mom + idx)) = gf4{b[0], b[1], b[2], b[3]};
+      } else {
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = g[p][u];
+      }
+#pragma unroll
+      for (int u = 0; u < 4; ++u) qs[lr][tc + u] = q[u];
+    }
+  } else {
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      const int lr = tr + 16 * p, sr = sr0 + lr, sc = sc0 + tc;
+      float q[4] = {0.f, 0.f, 0.f, 0.f};
+      if (sr < m) {
+        const int64_t idx = (int64_t)sr * n + sc;
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (sc + u < n) {
@@ -101,9 +117,9 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
           }
         }
       }
-    }
 #pragma unroll
-    for (int u = 0; u < 4; ++u) qs[lr][tc + u] = q[u];
+      for (int u = 0; u < 4; ++u) qs[lr][tc + u] = q[u];
+    }
   }
   __syncthreads();
 

@@ -155,9 +155,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   const int rp = d.rp, cp = d.cp;
   int ti, tj;
   if (OP == OP_APPLY) {
-    const int ntc = (cp + BN - 1) / BN;
-    ti = t / ntc;
-    tj = t % ntc;
+    // row blocks fastest: the tiles that run together share one X panel,
+    // and all B panels of a matrix (r x r) stay in L2 across column blocks,
+    // so each operand leaves HBM about once
+    const int ntr = (rp + BM - 1) / BM;
+    tj = t / ntr;
+    ti = t % ntr;
   } else {
     tri_decode(t, ti, tj);
   }
