@@ -8,7 +8,8 @@ every input already resident in HBM. Prints one JSON line.
 
 The Newton-Schulz figures use algorithmic FLOPs of what is computed: per
 iteration r(r+1)c for the Gram (one triangle), r(r+1)r for A^2 (one triangle)
-and 2r^2c for B X, per canonical r x c matrix.
+and 2r^2c for B X, per canonical r x c matrix. With the bf16 chain in one
+persistent launch (ns_persistent_bf16), a launch covers all iterations.
 """
 import argparse
 import json
@@ -49,6 +50,11 @@ def ns_flops_per_launch(mats):
     apply = sum(2 * r * r * c for r, c in mats)
     return {"ns_gram_bf16": gram, "ns_square_bf16": square, "ns_apply_bf16": apply,
             "ns_gram_f32": gram, "ns_square_f32": square, "ns_apply_f32": apply}
+
+
+def ns_flops_persistent(mats, steps):
+    """Algorithmic FLOPs of the single launch that runs every iteration."""
+    return sum(ns_flops(r, c, steps) for r, c in mats)
 
 
 def elementwise_bytes(wl):
@@ -190,6 +196,7 @@ def main():
 
     mats = [(min(m, n), max(m, n)) for (_, _, _, m, n) in wl.matrices()]
     fl = ns_flops_per_launch(mats)
+    fl["ns_persistent_bf16"] = ns_flops_persistent(mats, h.ns_steps)
     ns_total_flops = sum(ns_flops(r, c, h.ns_steps) for r, c in mats)
     by = elementwise_bytes(wl)
     kernels = {}

@@ -26,7 +26,7 @@ COPY_BYTES = 1 << 30
 
 # kernel symbol -> the name the library's per-kernel timing uses
 _NAMES = [
-    (r"ns_mfma_kernel<0>", "ns_gram_bf16"), (r"ns_mfma_kernel<1>", "ns_square_bf16"),
+    (r"ns_persistent_kernel", "ns_persistent_bf16"), (r"ns_mfma_kernel<0>", "ns_gram_bf16"), (r"ns_mfma_kernel<1>", "ns_square_bf16"),
     (r"ns_mfma_kernel<2>", "ns_apply_bf16"), (r"ns_f32_kernel<0>", "ns_gram_f32"),
     (r"ns_f32_kernel<1>", "ns_square_f32"), (r"ns_f32_kernel<2>", "ns_apply_f32"),
     (r"momentum_kernel", "momentum"), (r"norm_finalize_kernel", "norm_finalize"),

@@ -17,6 +17,7 @@
 #include <map>
 #include <mutex>
 #include <string>
+#include <cstdlib>
 #include <vector>
 
 #include "muon_adamw.h"
@@ -66,6 +67,13 @@ struct Plan {
   int gemm_tile = 128;
   std::vector<int32_t> ints;
   size_t desc_bytes = 0, table_bytes = 0, ws_bytes = 0;
+  // persistent Newton-Schulz launch (bf16): per-XCD segment lists in `ints`
+  // (int4 records from byte segs_off) and a zeroed counter region
+  bool persist = false;
+  size_t segs_off = 0, off_counters = 0;
+  int counter_ints = 0;
+  int32_t seg_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};
+  int32_t nseg[8] = {0, 0, 0, 0, 0, 0, 0, 0};
   MapRef ew, gram, sq, app, rows_nt, cols_t, rows_t, cols_nt, fin_all, out;
 };
 
@@ -76,6 +84,11 @@ struct Item {
 };
 
 constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
+// Steps with at most this many matrices run Newton-Schulz as one persistent
+// launch; the counter region grows by 128 bytes per matrix. The environment
+// variable MA_NS_SCHEDULE=launches selects three launches per iteration
+// instead (same tiles, plain kernel boundaries between the products).
+constexpr int kMaxPersistMats = 1 << 16;
 
 // Lays out a launch's tile list. Plain maps keep one list ordered by
 // decreasing per-tile work (the dispatcher then runs longest tiles first).
@@ -293,6 +306,40 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     P.gram = add_map(P, gram, &xcd_of);
     P.sq = add_map(P, sq, &xcd_of);
     P.app = add_map(P, app, &xcd_of);
+    // Queues of the persistent launch: per XCD, segments in (iteration,
+    // product, matrix) order, matrices longest first; a segment needs every
+    // earlier product of its matrix complete.
+    const char* sched = std::getenv("MA_NS_SCHEDULE");
+    const bool launches = sched && std::string(sched) == "launches";
+    if (nm <= kMaxPersistMats && !launches) {
+      P.persist = true;
+      while (P.ints.size() % 4) P.ints.push_back(0);
+      P.segs_off = P.ints.size() * sizeof(int32_t);
+      int32_t nrec = 0;
+      for (int x = 0; x < kXcds; ++x) {
+        std::vector<int> ms;
+        for (int k : order)
+          if (xcd_of[k] == x) ms.push_back(k);
+        P.seg_off[x] = nrec;
+        int32_t start = 0;
+        for (int it = 0; it < hp->ns_steps; ++it)
+          for (int op = 0; op < 3; ++op)
+            for (int k : ms) {
+              const int g = gram[k].tiles, q2 = sq[k].tiles, a = app[k].tiles;
+              const int tiles = op == 0 ? g : (op == 1 ? q2 : a);
+              const int64_t need = static_cast<int64_t>(it) * (g + q2 + a) + (op >= 1 ? g : 0) + (op >= 2 ? q2 : 0);
+              if (need > INT32_MAX || static_cast<int64_t>(start) + tiles > INT32_MAX)
+                return fail(MA_E_UNSUPPORTED, "Newton-Schulz task queue too long");
+              P.ints.insert(P.ints.end(), {k, it * 4 + op, start, static_cast<int32_t>(need)});
+              start += tiles;
+              ++nrec;
+            }
+        P.ints.insert(P.ints.end(), {0, 0, start, 0});   // sentinel: queue length
+        P.nseg[x] = nrec - P.seg_off[x];
+        ++nrec;
+      }
+      P.counter_ints = 8 * 32 + 32 + nm * 32;
+    }
   } else {
     P.gram = add_map(P, gram);
     P.sq = add_map(P, sq);
@@ -322,6 +369,10 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     mp.off_csc = off; off += align_up(static_cast<size_t>(mp.cp) * 4);
     mp.off_rf = off; off += align_up(static_cast<size_t>(mp.m) * 4);
     mp.off_cf = off; off += align_up(static_cast<size_t>(mp.n) * 4);
+  }
+  if (P.persist) {
+    P.off_counters = off;
+    off += align_up(static_cast<size_t>(P.counter_ints) * sizeof(int32_t));
   }
   P.ws_bytes = off;
   return MA_OK;
@@ -477,7 +528,20 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
   static const char* const kNsNames[2][3] = {{"ns_gram_f32", "ns_square_f32", "ns_apply_f32"},
                                              {"ns_gram_bf16", "ns_square_bf16", "ns_apply_bf16"}};
   const int bf = P.ns_dt == MA_BF16;
-  for (int it = 0; it < hp->ns_steps; ++it) {
+  if (P.persist) {
+    NsQueue q;
+    q.segs = reinterpret_cast<const int4*>(base + P.desc_bytes + P.segs_off);
+    q.qhead = reinterpret_cast<int*>(base + P.off_counters);
+    q.err = q.qhead + 8 * 32;
+    q.count = q.err + 32;
+    for (int x = 0; x < 8; ++x) {
+      q.seg_off[x] = P.seg_off[x];
+      q.nseg[x] = P.nseg[x];
+    }
+    timed("ns_persistent_bf16", s,
+          [&] { launch_ns_persistent(mats, q, P.counter_ints, hp->ns_a, hp->ns_b, hp->ns_c, s); });
+  }
+  for (int it = 0; it < (P.persist ? 0 : hp->ns_steps); ++it) {
     for (int op = NS_GRAM; op <= NS_APPLY; ++op) {
       const TileMap tm = TM(op == NS_APPLY ? P.app : (op == NS_GRAM ? P.gram : P.sq));
       timed(kNsNames[bf][op], s, [&] {

@@ -72,6 +72,23 @@ struct TileMap {
   int32_t xcnt[8];
 };
 
+// Task queues of the persistent Newton-Schulz launch: one per XCD.
+// segs[seg_off[x] .. seg_off[x] + nseg[x]] are XCD x's segments {matrix,
+// iteration * 4 + product, first task index, tiles of the matrix that must
+// be complete first}, followed by a sentinel whose .z is the queue length.
+// qhead (8 counters, 32 ints apart), err (1 int, then padding) and count
+// (one counter per matrix, 32 ints apart) are contiguous in that order and
+// zeroed by the launcher.
+constexpr int kPersistBlocksPerXcd = 32;   // one block per CU
+struct NsQueue {
+  const int4* segs;
+  int* qhead;
+  int* err;
+  int* count;
+  int32_t seg_off[8];
+  int32_t nseg[8];
+};
+
 __device__ __forceinline__ int find_entry(const TileMap& tm, int tile) {
   int lo = 0, hi = tm.nmat - 1;
   while (lo < hi) {

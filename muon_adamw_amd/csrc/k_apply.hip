@@ -67,13 +67,13 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
   // gradient) loads first, so they are in flight together with the loads of
   // U; edge tiles take the element-wise path below.
   const bool full = d.vec && s0 + kEw <= m && c0 + kEw <= n;
-  float w[4][4], g[4][4];
+  float wf[4][4], gf[4][4];
   if (full && mode != APPLY_COPY) {
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
       const int64_t idx = (int64_t)(s0 + tr + 16 * p) * n + c0 + tc;
-      load4v(d.param, idx, d.pdt, w[p]);
-      if (cautious == CAUT_WRAPPER) load4v(d.grad, idx, d.gdt, g[p]);
+      load4v(d.param, idx, d.pdt, wf[p]);
+      if (cautious == CAUT_WRAPPER) load4v(d.grad, idx, d.gdt, gf[p]);
     }
   }
 
@@ -110,18 +110,18 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
         for (int u = 0; u < 4; ++u) wn[u] = uu[u];
       } else if (cautious == CAUT_NONE) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) wn[u] = d.decay * w[p][u] - d.step * uu[u];
+        for (int u = 0; u < 4; ++u) wn[u] = d.decay * wf[p][u] - d.step * uu[u];
       } else if (cautious == CAUT_WD_MASK) {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          wn[u] = w[p][u] - d.step * uu[u];
-          if (uu[u] * w[p][u] >= 0.f) wn[u] -= d.lrwd * w[p][u];
+          wn[u] = wf[p][u] - d.step * uu[u];
+          if (uu[u] * wf[p][u] >= 0.f) wn[u] -= d.lrwd * wf[p][u];
         }
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-          const float delta = d.lrwd * w[p][u] + d.step * uu[u];
-          wn[u] = (delta * g[p][u] > 0.f) ? w[p][u] - delta : w[p][u];
+          const float delta = d.lrwd * wf[p][u] + d.step * uu[u];
+          wn[u] = (delta * gf[p][u] > 0.f) ? wf[p][u] - delta : wf[p][u];
         }
       }
       store4v(d.param, idx, d.pdt, wn);

@@ -143,15 +143,14 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
   return v;
 }
 
+// One 256 x 256 output tile `t` of product OP for matrix d. `src` is the
+// ping-pong buffer holding the current X, `first` folds in sigma. Every
+// thread of the block calls it; it ends with a barrier, after which LDS is
+// free again.
 template <int OP>
-__global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
-  __shared__ __attribute__((aligned(16))) char smem[SMEM];
-
-  const int t_all = block_tile(args.tm, blockIdx.x);
-  if (t_all < 0) return;
-  const int e = find_entry(args.tm, t_all);
-  const MatDesc& d = args.mats[args.tm.perm[e]];
-  const int t = t_all - args.tm.start[e];
+__device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int first, float coef_a, float coef_b,
+                                        float coef_c,
+                                        char* smem) {
   const int rp = d.rp, cp = d.cp;
   int ti, tj;
   if (OP == OP_APPLY) {
@@ -164,7 +163,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   } else {
     tri_decode(t, ti, tj);
   }
-  const uint16_t* Xin = static_cast<const uint16_t*>(args.src ? d.x1 : d.x0);
+  const uint16_t* Xin = static_cast<const uint16_t*>(src ? d.x1 : d.x0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 
   // Operand geometry.
@@ -342,7 +341,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
 
   // ---------------------------------------------------------------- epilogue
   float alpha = 1.f;
-  if (args.first) {
+  if (first) {
     const float sg = gmem(d.stat)[0];
     alpha = (OP == OP_GRAM) ? sg * sg : (OP == OP_APPLY ? sg : 1.f);
   }
@@ -354,7 +353,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   } else if (OP == OP_SQUARE) {
     out = static_cast<uint16_t*>(d.b); ldo = rp; limR = rp; limC = rp; extra = static_cast<const uint16_t*>(d.a);
   } else {
-    out = static_cast<uint16_t*>(args.src ? d.x0 : d.x1); ldo = cp; limR = rp; limC = cp; extra = Xin;
+    out = static_cast<uint16_t*>(src ? d.x0 : d.x1); ldo = cp; limR = rp; limC = cp; extra = Xin;
   }
 
   // Every load of the combine term reads a clamped, always valid address, so
@@ -404,7 +403,7 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
             float x[4];
             unpack4(xx[j][g], x);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
+            for (int u = 0; u < 4; ++u) v[u] = coef_b * x[u] + coef_c * v[u];
           }
           if (ok[j][g]) store4(go[j][g], v);
         }
@@ -454,10 +453,10 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
         unpack4(xx[it], x);
         if (OP == OP_SQUARE) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = args.b * x[u] + args.c * v[u];
+          for (int u = 0; u < 4; ++u) v[u] = coef_b * x[u] + coef_c * v[u];
         } else {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = alpha * (args.a * x[u] + v[u]);
+          for (int u = 0; u < 4; ++u) v[u] = alpha * (coef_a * x[u] + v[u]);
         }
       }
       if (ok[it]) store4(go[it], v);
@@ -466,7 +465,125 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   }
 }
 
+template <int OP>
+__global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  const int t_all = block_tile(args.tm, blockIdx.x);
+  if (t_all < 0) return;
+  const int e = find_entry(args.tm, t_all);
+  ns_tile<OP>(args.mats[args.tm.perm[e]], t_all - args.tm.start[e], args.src, args.first, args.a, args.b, args.c,
+              smem);
+}
+
+// All Newton-Schulz iterations of a step in one launch. Each XCD serves its
+// own queue (the workgroup reads the XCD it runs on from the XCC_ID
+// register): the matrices of a queue never leave that XCD, so everything a
+// tile reads was written through the same L2. A queue is a list of segments
+// {matrix, iteration*4 + product, first task, tiles of the matrix done
+// before}, in (iteration, product, matrix) order; a block takes the next
+// task, waits until the matrix's completion counter reaches the segment's
+// requirement (every earlier product of that matrix complete), runs the
+// tile and counts it. Tasks are taken in queue order, so a wait only ever
+// depends on tasks that running blocks already hold: the schedule cannot
+// deadlock. Each wait is still bounded (kMaxPolls, about a second); one that
+// runs out sets the error word, after which no wait blocks again, and the
+// block goes on: every wave always exits, and a broken schedule costs at
+// most one timeout.
+//
+// Visibility: a producer waits for its own stores (vmcnt(0)) before the
+// block's counter increment, so its tile is in L2 before the count moves;
+// a consumer invalidates its CU's L1 (buffer_inv at agent scope) after the
+// wait and before reading, since the CU may hold lines of the same matrix
+// from an earlier task. L2 is shared by producer and consumer (same XCD), so
+// nothing is written back. Counters are agent-scope atomics.
+constexpr int kMaxPolls = 1 << 20;
+
+__global__ __launch_bounds__(NTHR, 1) void ns_persistent_kernel(const MatDesc* __restrict__ mats, NsQueue q,
+                                                                float coef_a, float coef_b, float coef_c) {
+  __shared__ __attribute__((aligned(16))) char smem[SMEM];
+  __shared__ int task[4];
+  const int x = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;   // hwreg(HW_REG_XCC_ID, 0, 4)
+  const int4* segs = q.segs + q.seg_off[x];
+  const int nseg = q.nseg[x];
+  const int total = nseg ? segs[nseg].z : 0;   // sentinel segment holds the queue length
+  // Wave 0 fetches and waits; the branch on it is wave-uniform (a scalar
+  // branch), and every value it computes is made uniform with
+  // readfirstlane, so the task loop stays one loop for all lanes. (With a
+  // thread-0-only fetch the compiler split the loop per lane: the other
+  // lanes looped back to the barrier without ever fetching again.)
+  const bool wave0 = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6) == 0;
+  for (;;) {
+    if (wave0) {
+      int t = 0;
+      if (threadIdx.x == 0)
+        t = __hip_atomic_fetch_add(q.qhead + 32 * x, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+      t = __builtin_amdgcn_readfirstlane(t);
+      int m = -1, itop = 0, tile = 0;
+      if (t < total) {
+        int lo = 0, hi = nseg - 1;
+        while (lo < hi) {
+          const int mid = (lo + hi + 1) >> 1;
+          if (__builtin_amdgcn_readfirstlane(segs[mid].z) <= t) lo = mid; else hi = mid - 1;
+        }
+        const int4 sg = segs[lo];
+        m = __builtin_amdgcn_readfirstlane(sg.x);
+        itop = __builtin_amdgcn_readfirstlane(sg.y);
+        tile = t - __builtin_amdgcn_readfirstlane(sg.z);
+        const int need = __builtin_amdgcn_readfirstlane(sg.w);
+        for (int polls = 0;; ++polls) {
+          const int done = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(q.count + 32 * m, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (done >= need) break;
+          // after one wait has run out, no wait anywhere blocks again
+          const int failed = __builtin_amdgcn_readfirstlane(
+              __hip_atomic_load(q.err, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT));
+          if (failed || polls >= kMaxPolls) {
+            if (threadIdx.x == 0) __hip_atomic_store(q.err, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+            break;
+          }
+          __builtin_amdgcn_s_sleep(4);
+        }
+        // agent scope (sc1): the workgroup-scope form does not touch the L1
+        // outside thread-group-split mode, and this CU may hold lines of the
+        // matrix from an earlier task
+        asm volatile("buffer_inv sc1\n\ts_waitcnt vmcnt(0)" ::: "memory");
+      }
+      if (threadIdx.x == 0) {
+        task[0] = m;
+        task[1] = itop;
+        task[2] = tile;
+      }
+    }
+    __syncthreads();
+    const int m = __builtin_amdgcn_readfirstlane(task[0]);
+    const int itop = __builtin_amdgcn_readfirstlane(task[1]);
+    const int tile = __builtin_amdgcn_readfirstlane(task[2]);
+    if (m < 0) break;
+    const MatDesc& d = mats[m];
+    const int it = itop >> 2, op = itop & 3;
+    if (op == OP_GRAM)
+      ns_tile<OP_GRAM>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
+    else if (op == OP_SQUARE)
+      ns_tile<OP_SQUARE>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
+    else
+      ns_tile<OP_APPLY>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
+    asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
+    __syncthreads();
+    if (threadIdx.x == 0) __hip_atomic_fetch_add(q.count + 32 * m, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+  }
+}
+
+__global__ void zero_ints_kernel(int* p, int n) {
+  for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) gmem(p)[i] = 0;
+}
+
 }  // namespace
+
+void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, float a, float b, float c,
+                          hipStream_t s) {
+  hipLaunchKernelGGL(zero_ints_kernel, dim3(16), dim3(256), 0, s, q.qhead, zero_ints);
+  hipLaunchKernelGGL(ns_persistent_kernel, dim3(8 * kPersistBlocksPerXcd), dim3(NTHR), 0, s, mats, q, a, b, c);
+}
 
 void launch_ns_bf16(int op, const MatDesc* mats, TileMap tm, int src, int first, float a, float b, float c,
                     hipStream_t s) {

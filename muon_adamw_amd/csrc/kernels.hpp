@@ -21,6 +21,11 @@ void launch_ns_bf16(int op, const MatDesc* mats, TileMap tm, int src, int first,
                     hipStream_t s);
 void launch_ns_f32(int op, const MatDesc* mats, TileMap tm, int src, int first, float a, float b, float c,
                    hipStream_t s);
+// Every iteration of the bf16 Newton-Schulz chain in one persistent launch
+// (after zeroing the first `zero_ints` ints at q.qhead: the queue heads, the
+// error word and the completion counters).
+void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, float a, float b, float c,
+                          hipStream_t s);
 
 // Sums of squares of the final Newton-Schulz output along canonical rows
 // (csum_r) or canonical columns (csum_c), optionally weighted by the square

@@ -8,6 +8,7 @@ decay / cautious steps are fed the GPU's own Newton-Schulz output, and the
 parameters must then agree to fp32 rounding.
 """
 import math
+import os
 
 import numpy as np
 import pytest
@@ -398,3 +399,27 @@ def test_two_steps_continue_from_state():
         assert torch.equal(t.param, c.param) and torch.equal(t.momentum, c.momentum)
         check_momentum(t.momentum, w["momentum"])
         assert rel(host(t.param), w["W64"]) < 1e-5
+
+
+@pytest.mark.gpu
+def test_persistent_schedule_matches_launches():
+    """The one-launch Newton-Schulz schedule (per-XCD task queues with
+    completion counters) gives the same bits as three launches per iteration,
+    run after run: every tile reads only data its producers finished."""
+    flush("persistent vs launches")
+    xs = [randn((4, 768, 768), 91).to(torch.bfloat16), randn((768, 3072), 92).to(torch.bfloat16),
+          randn((300, 200), 93).to(torch.bfloat16)]
+    hp = ma.muon_hparams(ns_dtype="bf16")
+    outs = {}
+    for sched in ("launches", "persistent"):
+        os.environ["MA_NS_SCHEDULE"] = sched
+        try:
+            outs[sched] = [[ma.newton_schulz(x.to(DEV), hp).cpu() for _ in range(2)] for x in xs]
+        finally:
+            del os.environ["MA_NS_SCHEDULE"]
+    torch.cuda.synchronize()
+    for i in range(len(xs)):
+        ref = outs["launches"][i][0].view(torch.int16)
+        for sched in ("launches", "persistent"):
+            for o in outs[sched][i]:
+                assert torch.equal(o.view(torch.int16), ref), (i, sched)
