@@ -19,18 +19,19 @@ template <typename XT>
 __device__ __forceinline__ void load4(const XT* p, float* v);
 template <>
 __device__ __forceinline__ void load4<float>(const float* p, float* v) {
-  const gf4 x = *gmem(reinterpret_cast<const gf4*>(p));
+  const gf4 x = __builtin_nontemporal_load(gmem(reinterpret_cast<const gf4*>(p)));
   v[0] = x.x; v[1] = x.y; v[2] = x.z; v[3] = x.w;
 }
 template <>
 __device__ __forceinline__ void load4<uint16_t>(const uint16_t* p, float* v) {
-  const gu2 x = *gmem(reinterpret_cast<const gu2*>(p));
+  const gu2 x = __builtin_nontemporal_load(gmem(reinterpret_cast<const gu2*>(p)));
   v[0] = __uint_as_float(x.x << 16); v[1] = __uint_as_float(x.x & 0xffff0000u);
   v[2] = __uint_as_float(x.y << 16); v[3] = __uint_as_float(x.y & 0xffff0000u);
 }
 
 // Four consecutive stored elements (the caller guarantees 16-byte alignment
 // for fp32 and 8-byte alignment for bf16 via the descriptor's vec flag).
+// The vector accesses of U, W and G are nontemporal: each is touched once.
 __device__ __forceinline__ void load4v(const void* p, int64_t i, int dt, float* v) {
   if (dt == DT_BF16) {
     load4<uint16_t>(static_cast<const uint16_t*>(p) + i, v);
@@ -43,9 +44,9 @@ __device__ __forceinline__ void store4v(void* p, int64_t i, int dt, const float*
     gu2 x;
     x.x = pack_bf16x2(v[0], v[1]);
     x.y = pack_bf16x2(v[2], v[3]);
-    *gmem(reinterpret_cast<gu2*>(static_cast<uint16_t*>(p) + i)) = x;
+    __builtin_nontemporal_store(x, gmem(reinterpret_cast<gu2*>(static_cast<uint16_t*>(p) + i)));
   } else {
-    *gmem(reinterpret_cast<gf4*>(static_cast<float*>(p) + i)) = gf4{v[0], v[1], v[2], v[3]};
+    __builtin_nontemporal_store(gf4{v[0], v[1], v[2], v[3]}, gmem(reinterpret_cast<gf4*>(static_cast<float*>(p) + i)));
   }
 }
 

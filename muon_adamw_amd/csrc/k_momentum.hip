@@ -58,6 +58,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
   // Phase 1: stored tile, coalesced along stored rows. A full, aligned tile
   // (the common case) issues all of a thread's loads before any use, so
   // they are in flight together; edge tiles take the element-wise path.
+  // G and B are touched once per step: nontemporal accesses. Q stays
+  // cached, since Newton-Schulz reads it next.
   const bool full = d.vec && sr0 + kEw <= m && sc0 + kEw <= n;
   if (full) {
     float g[4][4];
@@ -66,14 +68,14 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
     for (int p = 0; p < 4; ++p) {
       const int64_t idx = (int64_t)(sr0 + tr + 16 * p) * n + sc0 + tc;
       if (d.gdt == DT_BF16) {
-        const gu2 raw = *gmem(reinterpret_cast<const gu2*>(static_cast<const uint16_t*>(d.grad) + idx));
+        const gu2 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const gu2*>(static_cast<const uint16_t*>(d.grad) + idx)));
         g[p][0] = __uint_as_float(raw.x << 16); g[p][1] = __uint_as_float(raw.x & 0xffff0000u);
         g[p][2] = __uint_as_float(raw.y << 16); g[p][3] = __uint_as_float(raw.y & 0xffff0000u);
       } else {
-        const gf4 raw = *gmem(reinterpret_cast<const gf4*>(static_cast<const float*>(d.grad) + idx));
+        const gf4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const gf4*>(static_cast<const float*>(d.grad) + idx)));
         g[p][0] = raw.x; g[p][1] = raw.y; g[p][2] = raw.z; g[p][3] = raw.w;
       }
-      if (d.mom) bm[p] = *gmem(reinterpret_cast<const gf4*>(d.mom + idx));
+      if (d.mom) bm[p] = __builtin_nontemporal_load(gmem(reinterpret_cast<const gf4*>(d.mom + idx)));
     }
 #pragma unroll
     for (int p = 0; p < 4; ++p) {
@@ -87,7 +89,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
           b[u] = beta * b[u] + omb * g[p][u];
           q[u] = nesterov ? g[p][u] + beta * (b[u] - g[p][u]) : b[u];
         }
-        *gmem(reinterpret_cast<gf4*>(d.mom + idx)) = gf4{b[0], b[1], b[2], b[3]};
+        __builtin_nontemporal_store(gf4{b[0], b[1], b[2], b[3]}, gmem(reinterpret_cast<gf4*>(d.mom + idx)));
       } else {
 #pragma unroll
         for (int u = 0; u < 4; ++u) q[u] = g[p][u];

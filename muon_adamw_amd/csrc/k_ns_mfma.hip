@@ -128,6 +128,45 @@ __device__ __forceinline__ void tri_decode(int k, int& ti, int& tj) {
   tj = k - i * (i + 1) / 2;
 }
 
+// Tile orders. The tiles of one matrix run on one XCD, about 32 at a time,
+// so consecutive tiles should cover a compact area of the output and share
+// operand panels in that XCD's L2.
+// Symmetric products (lower triangle, ntr block rows): groups of kTriGroup
+// block rows in order; inside a group, column by column with the rows of the
+// group fastest. A group spans the same positions as in plain row-major
+// order, so the group of position t is the row-major row of t over kTriGroup.
+constexpr int kTriGroup = 4;
+__device__ __forceinline__ void tri_decode_grouped(int t, int ntr, int& ti, int& tj) {
+  int i, j;
+  tri_decode(t, i, j);
+  const int r0 = (i / kTriGroup) * kTriGroup, gsz = min(kTriGroup, ntr - r0);
+  int u = t - r0 * (r0 + 1) / 2;
+  if (u < r0 * gsz) {            // columns left of the group's diagonal block: full height
+    tj = u / gsz;
+    ti = r0 + u % gsz;
+    return;
+  }
+  u -= r0 * gsz;                 // the diagonal block: column c has gsz - c rows
+  int c = 0;
+  while (u >= gsz - c) {
+    u -= gsz - c;
+    ++c;
+  }
+  tj = r0 + c;
+  ti = r0 + c + u;
+}
+// APPLY (ntr x ntc tiles): groups of kApplyGroup block rows; inside a group
+// the rows are fastest, so about 32 consecutive tiles cover 8 rows x 4
+// columns. With ntr <= kApplyGroup this is plain column-major order, in which
+// all of B (r x r) serves every column block from L2.
+constexpr int kApplyGroup = 8;
+__device__ __forceinline__ void apply_decode(int t, int ntr, int ntc, int& ti, int& tj) {
+  const int r0 = (t / (kApplyGroup * ntc)) * kApplyGroup, gsz = min(kApplyGroup, ntr - r0);
+  const int u = t - r0 * ntc;
+  ti = r0 + u % gsz;
+  tj = u / gsz;
+}
+
 __device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
   f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
@@ -153,16 +192,11 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
                                         char* smem) {
   const int rp = d.rp, cp = d.cp;
   int ti, tj;
-  if (OP == OP_APPLY) {
-    // row blocks fastest: the tiles that run together share one X panel,
-    // and all B panels of a matrix (r x r) stay in L2 across column blocks,
-    // so each operand leaves HBM about once
-    const int ntr = (rp + BM - 1) / BM;
-    tj = t / ntr;
-    ti = t % ntr;
-  } else {
-    tri_decode(t, ti, tj);
-  }
+  const int ntr = (rp + BM - 1) / BM;
+  if (OP == OP_APPLY)
+    apply_decode(t, ntr, (cp + BN - 1) / BN, ti, tj);
+  else
+    tri_decode_grouped(t, ntr, ti, tj);
   const uint16_t* Xin = static_cast<const uint16_t*>(src ? d.x1 : d.x0);
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
 

@@ -56,7 +56,7 @@ struct AdamTensorArg {
   float lr, wd;
 };
 constexpr int kMaxAdamTensors = 32;
-constexpr int kAdamChunk = 8192;  // elements per block
+constexpr int kAdamChunk = 2048;  // elements per block
 struct AdamLaunch {
   AdamTensorArg t[kMaxAdamTensors];
   int32_t block_start[kMaxAdamTensors + 1];
