@@ -223,6 +223,10 @@ typedef struct {
   uint64_t u_offset;     /* workspace byte offset of the final Newton-Schulz
                             output: rp x cp row-major, ns dtype, canonical
                             orientation, zero outside r x c                   */
+  uint64_t a_offset;     /* workspace byte offset of the last iteration's
+                            A = X X^T: rp x rp row-major, ns dtype, both
+                            triangles stored (bit for bit equal)              */
+  uint64_t b_offset;     /* the same for B = bA + cA^2                        */
 } ma_matrix_info;
 
 /* Number of matrices and shape buckets muon_step would form (host only). */

@@ -62,7 +62,7 @@ class MatrixInfoC(ctypes.Structure):
                 ("r", ctypes.c_int32), ("c", ctypes.c_int32), ("rp", ctypes.c_int32),
                 ("cp", ctypes.c_int32), ("transposed", ctypes.c_int32),
                 ("bucket", ctypes.c_int32), ("scale", ctypes.c_float), ("pad_", ctypes.c_int32),
-                ("u_offset", ctypes.c_uint64)]
+                ("u_offset", ctypes.c_uint64), ("a_offset", ctypes.c_uint64), ("b_offset", ctypes.c_uint64)]
 
 
 class KernelTimeC(ctypes.Structure):

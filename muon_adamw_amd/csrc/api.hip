@@ -692,6 +692,8 @@ ma_status ma_muon_matrix_info(const ma_muon_tensor* tensors, int32_t n, const ma
   info->bucket = mp.bucket;
   info->scale = mp.scale;
   info->u_offset = (hp->ns_steps & 1) ? mp.off_x1 : mp.off_x0;
+  info->a_offset = mp.off_a;
+  info->b_offset = mp.off_b;
   return MA_OK;
 }
 

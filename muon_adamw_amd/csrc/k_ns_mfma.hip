@@ -167,6 +167,13 @@ __device__ __forceinline__ void apply_decode(int t, int ntr, int ntc, int& ti, i
   tj = u / gsz;
 }
 
+// b A + c A^2 for one element, in one fixed rounding order. The direct and
+// the mirrored tile of SQUARE both use it, so B is symmetric bit for bit
+// (left to the compiler, the two paths fused different products).
+__device__ __forceinline__ float square_combine(float a, float a2, float b, float c) {
+  return __builtin_fmaf(c, a2, b * a);
+}
+
 __device__ __forceinline__ void unpack8(const u32x4& v, float* f) {
   f[0] = __uint_as_float(v.x << 16); f[1] = __uint_as_float(v.x & 0xffff0000u);
   f[2] = __uint_as_float(v.y << 16); f[3] = __uint_as_float(v.y & 0xffff0000u);
@@ -214,23 +221,34 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
   }
   const int nk = K / BK;
 
-  // Direct loads of a contraction-contiguous operand: wave w fills tile rows
-  // [32w, 32w+32) with two 16-row instructions; lane l takes LDS slot
-  // (row 16i + l/4, slot l%4) and loads the chunk the swizzle places there.
-  const int drow0 = 32 * w + (lane >> 2), drow1 = drow0 + 16;
-  const int dch0 = (lane & 3) ^ swz(drow0), dch1 = (lane & 3) ^ swz(drow1);
-  const uint16_t* ga0 = Abase + (int64_t)min(ti * BM + drow0, limA - 1) * lda + dch0 * 8;
-  const uint16_t* ga1 = Abase + (int64_t)min(ti * BM + drow1, limA - 1) * lda + dch1 * 8;
-  const uint16_t* gb0;
-  const uint16_t* gb1;
-  if (OP != OP_APPLY) {
+  // Operand layout in LDS. GRAM's operands are rows of X, read along the
+  // contraction (64-byte rows per stage). SQUARE and APPLY read both
+  // operands k-major (512-byte k-rows per stage): the second operand is
+  // stored that way, and the first is a symmetric matrix (A, B) whose
+  // stored row k holds column k, so its tile rows are read as columns of
+  // its k-rows. Every element read is the same value as in the row-wise
+  // reading. Measured on gfx950, direct loads of 512-byte (or 128-byte) row
+  // pieces stream from L2 about 1.7x faster than 64-byte pieces, which
+  // cannot keep up with the matrix cores.
+  constexpr bool KM = OP != OP_GRAM;
+  const uint16_t *ga0, *ga1, *gb0, *gb1;
+  if (!KM) {
+    // wave w fills tile rows [32w, 32w+32) with two 16-row instructions;
+    // lane l takes LDS slot (row 16i + l/4, slot l%4) and loads the chunk
+    // the swizzle places there
+    const int drow0 = 32 * w + (lane >> 2), drow1 = drow0 + 16;
+    const int dch0 = (lane & 3) ^ swz(drow0), dch1 = (lane & 3) ^ swz(drow1);
+    ga0 = Abase + (int64_t)min(ti * BM + drow0, limA - 1) * lda + dch0 * 8;
+    ga1 = Abase + (int64_t)min(ti * BM + drow1, limA - 1) * lda + dch1 * 8;
     gb0 = Bbase + (int64_t)min(tj * BN + drow0, limB - 1) * ldb + dch0 * 8;
     gb1 = Bbase + (int64_t)min(tj * BN + drow1, limB - 1) * ldb + dch1 * 8;
   } else {
-    // X: wave w fills k-rows 4w..4w+3, two rows (2 x 512 B) per instruction;
-    // lane l takes row 4w + 2i + l/32, slot l%32.
+    // wave w fills k-rows 4w..4w+3, two rows (2 x 512 B) per instruction;
+    // lane l takes row 4w + 2i + l/32, slot l%32
     const int xr0 = 4 * w + (lane >> 5), xr1 = xr0 + 2;
     const int xc0 = (lane & 31) ^ xswz(xr0), xc1 = (lane & 31) ^ xswz(xr1);
+    ga0 = Abase + (int64_t)xr0 * lda + min(ti * BM + xc0 * 8, limA - 8);
+    ga1 = Abase + (int64_t)xr1 * lda + min(ti * BM + xc1 * 8, limA - 8);
     gb0 = Bbase + (int64_t)xr0 * ldb + min(tj * BN + xc0 * 8, limB - 8);
     gb1 = Bbase + (int64_t)xr1 * ldb + min(tj * BN + xc1 * 8, limB - 8);
   }
@@ -246,39 +264,45 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
     const int ks = min(stage, nk - 1);
     const int64_t koffA = (int64_t)ks * BK;
     const uint32_t a = a_lds + buf * OPB, b = b_lds + buf * OPB;
-    dma16(ga0 + koffA, a);
-    dma16(ga1 + koffA, a + 16 * RB);
-    if (OP != OP_APPLY) {
+    if (!KM) {
+      dma16(ga0 + koffA, a);
+      dma16(ga1 + koffA, a + 16 * RB);
       dma16(gb0 + koffA, b);
       dma16(gb1 + koffA, b + 16 * RB);
     } else {
-      const int64_t koffX = (int64_t)ks * BK * ldb;
-      dma16(gb0 + koffX, b);
-      dma16(gb1 + koffX, b + 2 * XR);
+      dma16(ga0 + koffA * lda, a);
+      dma16(ga1 + koffA * lda, a + 2 * XR);
+      dma16(gb0 + koffA * ldb, b);
+      dma16(gb1 + koffA * ldb, b + 2 * XR);
     }
   };
 
   const int wr = w >> 2, wc = w & 3, khalf = lane >> 5;
-  // Per-lane LDS offsets of the fragments, [k-substep]: A rows, NT B rows.
-  int aoff[4][2], boff[2][2];
+  // Per-lane LDS offsets of the fragments. Row-wise operands, [k-substep]:
+  // A rows, NT B rows. k-major operands: the k-row and column a lane's
+  // transposing read starts at (k0 = 0); the other reads of a stage are
+  // whole-row shifts of it, because the swizzle depends on k mod 4 only.
+  int aoff[4][2] = {}, boff[2][2] = {}, akm[4] = {}, bkm[2] = {};
+  if (!KM) {
 #pragma unroll
-  for (int q = 0; q < 2; ++q) {
+    for (int q = 0; q < 2; ++q) {
 #pragma unroll
-    for (int i = 0; i < 4; ++i) aoff[i][q] = lds_off(wr * 128 + i * 32 + (lane & 31), q * 2 + khalf);
+      for (int i = 0; i < 4; ++i) aoff[i][q] = lds_off(wr * 128 + i * 32 + (lane & 31), q * 2 + khalf);
 #pragma unroll
-    for (int j = 0; j < 2; ++j) boff[j][q] = lds_off(wc * 64 + j * 32 + (lane & 31), q * 2 + khalf);
-  }
-  // APPLY's X fragments: offset of the k-row/column a lane's transposing read
-  // starts at (k0 = 0); the other reads of a stage are whole-row shifts of
-  // it, because the swizzle depends on k mod 4 only.
-  int xoffs[2] = {0, 0};
-  if (OP == OP_APPLY) {
+      for (int j = 0; j < 2; ++j) boff[j][q] = lds_off(wc * 64 + j * 32 + (lane & 31), q * 2 + khalf);
+    }
+  } else {
     const int q16 = lane >> 4, i16 = lane & 15;
+    const int k = 8 * (q16 >> 1) + (i16 >> 2);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int mm = wr * 128 + i * 32 + 16 * (q16 & 1) + 4 * (i16 & 3);
+      akm[i] = xoff(k, mm >> 3) + (mm & 7) * 2;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wc * 64 + j * 32 + 16 * (q16 & 1) + 4 * (i16 & 3);
-      const int k = 8 * (q16 >> 1) + (i16 >> 2);
-      xoffs[j] = xoff(k, n >> 3) + (n & 7) * 2;
+      bkm[j] = xoff(k, n >> 3) + (n & 7) * 2;
     }
   }
 
@@ -300,28 +324,28 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
   };
   Frag F0, F1;
 
+  // a k-major fragment: two transposing reads of four k-rows each
+  auto tr8 = [](const char* p) {
+    const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p));
+    const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((__attribute__((address_space(3))) i16x4*)(p + 4 * XR));
+    const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+    return __builtin_bit_cast(bf16x8, v);
+  };
   auto read = [&](Frag& f, int soff, auto Q_) {   // soff: byte offset of the stage's buffer
     constexpr int Q = decltype(Q_)::value;
     const char* As = Abuf + soff;
     const char* Bs = Bbuf + soff;
-    if constexpr (OP == OP_APPLY) {
+    if constexpr (KM) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) {
-        const char* p = Bs + xoffs[j] + Q * 16 * XR;
-        const i16x4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(p));
-        const i16x4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16(
-            (__attribute__((address_space(3))) i16x4*)(p + 4 * XR));
-        const short __attribute__((ext_vector_type(8))) v = {lo[0], lo[1], lo[2], lo[3],
-                                                             hi[0], hi[1], hi[2], hi[3]};
-        f.b[j] = __builtin_bit_cast(bf16x8, v);
-      }
+      for (int j = 0; j < 2; ++j) f.b[j] = tr8(Bs + bkm[j] + Q * 16 * XR);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) f.a[i] = tr8(As + akm[i] + Q * 16 * XR);
     } else {
 #pragma unroll
       for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + boff[j][Q]);
-    }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(As + aoff[i][Q]);
+      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(As + aoff[i][Q]);
+    }
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -437,7 +461,7 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
             float x[4];
             unpack4(xx[j][g], x);
 #pragma unroll
-            for (int u = 0; u < 4; ++u) v[u] = coef_b * x[u] + coef_c * v[u];
+            for (int u = 0; u < 4; ++u) v[u] = square_combine(x[u], v[u], coef_b, coef_c);
           }
           if (ok[j][g]) store4(go[j][g], v);
         }
@@ -487,7 +511,7 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
         unpack4(xx[it], x);
         if (OP == OP_SQUARE) {
 #pragma unroll
-          for (int u = 0; u < 4; ++u) v[u] = coef_b * x[u] + coef_c * v[u];
+          for (int u = 0; u < 4; ++u) v[u] = square_combine(x[u], v[u], coef_b, coef_c);
         } else {
 #pragma unroll
           for (int u = 0; u < 4; ++u) v[u] = alpha * (coef_a * x[u] + v[u]);

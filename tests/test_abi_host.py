@@ -58,6 +58,7 @@ int main(void) {{
   S(ma_adamw_tensor); O(ma_adamw_tensor, numel); O(ma_adamw_tensor, weight_decay);
   S(ma_adamw_hparams); O(ma_adamw_hparams, step);
   S(ma_matrix_info); O(ma_matrix_info, scale); O(ma_matrix_info, u_offset);
+  O(ma_matrix_info, a_offset); O(ma_matrix_info, b_offset);
   return 0;
 }}''')
     exe = tmp_path / "layout"
@@ -82,6 +83,8 @@ int main(void) {{
         "ma_matrix_info": ctypes.sizeof(ma.MatrixInfoC),
         "ma_matrix_info.scale": ma.MatrixInfoC.scale.offset,
         "ma_matrix_info.u_offset": ma.MatrixInfoC.u_offset.offset,
+        "ma_matrix_info.a_offset": ma.MatrixInfoC.a_offset.offset,
+        "ma_matrix_info.b_offset": ma.MatrixInfoC.b_offset.offset,
     }
     for k, v in want.items():
         assert int(got[k]) == v, (k, got[k], v)
