@@ -70,6 +70,7 @@ struct Plan {
   // persistent Newton-Schulz launch (bf16): per-XCD segment lists in `ints`
   // (int4 records from byte segs_off) and a zeroed counter region
   bool persist = false;
+  int operands = 0;   // 0: by size (k-major up to kKmajorMaxRows), 1: k-major, 2: row-wise
   size_t segs_off = 0, off_counters = 0;
   int counter_ints = 0;
   int32_t seg_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -89,6 +90,11 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
 // variable MA_NS_SCHEDULE=launches selects three launches per iteration
 // instead (same tiles, plain kernel boundaries between the products).
 constexpr int kMaxPersistMats = 1 << 16;
+// SQUARE and APPLY of matrices with at most this many (padded) rows read
+// both operands k-major; larger ones read their symmetric operand row-wise.
+// MA_NS_OPERANDS=kmajor or =rows forces one layout (the results are the same
+// bits either way).
+constexpr int kKmajorMaxRows = 2048;
 
 // Lays out a launch's tile list. Plain maps keep one list ordered by
 // decreasing per-tile work (the dispatcher then runs longest tiles first).
@@ -309,6 +315,8 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     // Queues of the persistent launch: per XCD, segments in (iteration,
     // product, matrix) order, matrices longest first; a segment needs every
     // earlier product of its matrix complete.
+    const char* opnd = std::getenv("MA_NS_OPERANDS");
+    P.operands = opnd && std::string(opnd) == "kmajor" ? 1 : (opnd && std::string(opnd) == "rows" ? 2 : 0);
     const char* sched = std::getenv("MA_NS_SCHEDULE");
     const bool launches = sched && std::string(sched) == "launches";
     if (nm <= kMaxPersistMats && !launches) {
@@ -512,6 +520,7 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
     d.rfac = reinterpret_cast<float*>(base + mp.off_rf);
     d.cfac = reinterpret_cast<float*>(base + mp.off_cf);
     d.ntile_ew = mp.ntile_ew;
+    d.kmajor = P.operands == 1 || (P.operands == 0 && mp.rp <= kKmajorMaxRows);
   }
   std::memcpy(host.data() + P.desc_bytes, P.ints.data(), P.ints.size() * sizeof(int32_t));
   ma_status st = upload(host, ws, s);

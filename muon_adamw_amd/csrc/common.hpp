@@ -51,7 +51,7 @@ struct MatDesc {
   float* rfac;        // per stored row factor, m entries
   float* cfac;        // per stored column factor, n entries
   int32_t ntile_ew;   // number of momentum-pass tiles (= partial count)
-  int32_t pad_;
+  int32_t kmajor;     // SQUARE and APPLY read both operands k-major (else row-wise)
 };
 
 // Maps a flat block index to (matrix, local tile) for one launch: matrices

@@ -193,10 +193,11 @@ __device__ __forceinline__ u32x4 pack8(const float* f) {
 // ping-pong buffer holding the current X, `first` folds in sigma. Every
 // thread of the block calls it; it ends with a barrier, after which LDS is
 // free again.
-template <int OP>
+template <int OP, bool KM>
 __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int first, float coef_a, float coef_b,
                                         float coef_c,
                                         char* smem) {
+  static_assert(!(OP == OP_GRAM && KM), "GRAM reads rows of X");
   const int rp = d.rp, cp = d.cp;
   int ti, tj;
   const int ntr = (rp + BM - 1) / BM;
@@ -221,16 +222,19 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
   }
   const int nk = K / BK;
 
-  // Operand layout in LDS. GRAM's operands are rows of X, read along the
-  // contraction (64-byte rows per stage). SQUARE and APPLY read both
-  // operands k-major (512-byte k-rows per stage): the second operand is
-  // stored that way, and the first is a symmetric matrix (A, B) whose
-  // stored row k holds column k, so its tile rows are read as columns of
-  // its k-rows. Every element read is the same value as in the row-wise
-  // reading. Measured on gfx950, direct loads of 512-byte (or 128-byte) row
-  // pieces stream from L2 about 1.7x faster than 64-byte pieces, which
-  // cannot keep up with the matrix cores.
-  constexpr bool KM = OP != OP_GRAM;
+  // Operand layout in LDS. Row-wise (KM false): each operand's tile rows
+  // are read along the contraction, 64-byte rows per stage; APPLY's X is
+  // k-major regardless, since it is stored that way. k-major (KM, SQUARE and
+  // APPLY): both operands as 512-byte k-rows per stage. The first operand
+  // is a symmetric matrix (A, B) whose two triangles are stored bit for bit
+  // equal, so its tile rows are read as columns of its k-rows and every
+  // element read is the same value as in the row-wise reading. On gfx950
+  // direct loads of 512-byte row pieces stream from L2 about 1.7x faster
+  // than 64-byte pieces, but the transposing LDS reads take twice the
+  // instructions of 16-byte row reads; the planner picks k-major for small
+  // matrices, where the operand stream limits (768 rows: 3% faster), and
+  // row-wise for large ones, where the chip runs power-limited and the extra
+  // LDS instructions cost clock (8192 rows: 6% slower k-major).
   const uint16_t *ga0, *ga1, *gb0, *gb1;
   if (!KM) {
     // wave w fills tile rows [32w, 32w+32) with two 16-row instructions;
@@ -240,8 +244,15 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
     const int dch0 = (lane & 3) ^ swz(drow0), dch1 = (lane & 3) ^ swz(drow1);
     ga0 = Abase + (int64_t)min(ti * BM + drow0, limA - 1) * lda + dch0 * 8;
     ga1 = Abase + (int64_t)min(ti * BM + drow1, limA - 1) * lda + dch1 * 8;
-    gb0 = Bbase + (int64_t)min(tj * BN + drow0, limB - 1) * ldb + dch0 * 8;
-    gb1 = Bbase + (int64_t)min(tj * BN + drow1, limB - 1) * ldb + dch1 * 8;
+    if (OP != OP_APPLY) {
+      gb0 = Bbase + (int64_t)min(tj * BN + drow0, limB - 1) * ldb + dch0 * 8;
+      gb1 = Bbase + (int64_t)min(tj * BN + drow1, limB - 1) * ldb + dch1 * 8;
+    } else {
+      const int xr0 = 4 * w + (lane >> 5), xr1 = xr0 + 2;
+      const int xc0 = (lane & 31) ^ xswz(xr0), xc1 = (lane & 31) ^ xswz(xr1);
+      gb0 = Bbase + (int64_t)xr0 * ldb + min(tj * BN + xc0 * 8, limB - 8);
+      gb1 = Bbase + (int64_t)xr1 * ldb + min(tj * BN + xc1 * 8, limB - 8);
+    }
   } else {
     // wave w fills k-rows 4w..4w+3, two rows (2 x 512 B) per instruction;
     // lane l takes row 4w + 2i + l/32, slot l%32
@@ -267,8 +278,13 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
     if (!KM) {
       dma16(ga0 + koffA, a);
       dma16(ga1 + koffA, a + 16 * RB);
-      dma16(gb0 + koffA, b);
-      dma16(gb1 + koffA, b + 16 * RB);
+      if (OP != OP_APPLY) {
+        dma16(gb0 + koffA, b);
+        dma16(gb1 + koffA, b + 16 * RB);
+      } else {
+        dma16(gb0 + koffA * ldb, b);
+        dma16(gb1 + koffA * ldb, b + 2 * XR);
+      }
     } else {
       dma16(ga0 + koffA * lda, a);
       dma16(ga1 + koffA * lda, a + 2 * XR);
@@ -283,26 +299,26 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
   // transposing read starts at (k0 = 0); the other reads of a stage are
   // whole-row shifts of it, because the swizzle depends on k mod 4 only.
   int aoff[4][2] = {}, boff[2][2] = {}, akm[4] = {}, bkm[2] = {};
-  if (!KM) {
-#pragma unroll
-    for (int q = 0; q < 2; ++q) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) aoff[i][q] = lds_off(wr * 128 + i * 32 + (lane & 31), q * 2 + khalf);
-#pragma unroll
-      for (int j = 0; j < 2; ++j) boff[j][q] = lds_off(wc * 64 + j * 32 + (lane & 31), q * 2 + khalf);
-    }
-  } else {
+  constexpr bool BKM = KM || OP == OP_APPLY;   // second operand k-major
+  {
     const int q16 = lane >> 4, i16 = lane & 15;
     const int k = 8 * (q16 >> 1) + (i16 >> 2);
 #pragma unroll
+    for (int q = 0; q < 2; ++q)
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (!KM) aoff[i][q] = lds_off(wr * 128 + i * 32 + (lane & 31), q * 2 + khalf);
+        if (!BKM && i < 2) boff[i][q] = lds_off(wc * 64 + i * 32 + (lane & 31), q * 2 + khalf);
+      }
+#pragma unroll
     for (int i = 0; i < 4; ++i) {
       const int mm = wr * 128 + i * 32 + 16 * (q16 & 1) + 4 * (i16 & 3);
-      akm[i] = xoff(k, mm >> 3) + (mm & 7) * 2;
+      if (KM) akm[i] = xoff(k, mm >> 3) + (mm & 7) * 2;
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int n = wc * 64 + j * 32 + 16 * (q16 & 1) + 4 * (i16 & 3);
-      bkm[j] = xoff(k, n >> 3) + (n & 7) * 2;
+      if (BKM) bkm[j] = xoff(k, n >> 3) + (n & 7) * 2;
     }
   }
 
@@ -335,17 +351,12 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
     constexpr int Q = decltype(Q_)::value;
     const char* As = Abuf + soff;
     const char* Bs = Bbuf + soff;
-    if constexpr (KM) {
 #pragma unroll
-      for (int j = 0; j < 2; ++j) f.b[j] = tr8(Bs + bkm[j] + Q * 16 * XR);
+    for (int j = 0; j < 2; ++j)
+      f.b[j] = BKM ? tr8(Bs + bkm[j] + Q * 16 * XR) : *reinterpret_cast<const bf16x8*>(Bs + boff[j][Q]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) f.a[i] = tr8(As + akm[i] + Q * 16 * XR);
-    } else {
-#pragma unroll
-      for (int j = 0; j < 2; ++j) f.b[j] = *reinterpret_cast<const bf16x8*>(Bs + boff[j][Q]);
-#pragma unroll
-      for (int i = 0; i < 4; ++i) f.a[i] = *reinterpret_cast<const bf16x8*>(As + aoff[i][Q]);
-    }
+    for (int i = 0; i < 4; ++i)
+      f.a[i] = KM ? tr8(As + akm[i] + Q * 16 * XR) : *reinterpret_cast<const bf16x8*>(As + aoff[i][Q]);
   };
   auto mma = [&](const Frag& f) {
 #pragma unroll
@@ -523,14 +534,28 @@ __device__ __forceinline__ void ns_tile(const MatDesc& d, int t, int src, int fi
   }
 }
 
+// The operand layout is chosen per matrix (MatDesc::kmajor, uniform).
+template <int OP>
+__device__ __forceinline__ void ns_tile_any(const MatDesc& d, int t, int src, int first, float coef_a,
+                                            float coef_b, float coef_c, char* smem) {
+  if constexpr (OP == OP_GRAM) {
+    ns_tile<OP, false>(d, t, src, first, coef_a, coef_b, coef_c, smem);
+  } else {
+    if (__builtin_amdgcn_readfirstlane(d.kmajor))
+      ns_tile<OP, true>(d, t, src, first, coef_a, coef_b, coef_c, smem);
+    else
+      ns_tile<OP, false>(d, t, src, first, coef_a, coef_b, coef_c, smem);
+  }
+}
+
 template <int OP>
 __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   const int t_all = block_tile(args.tm, blockIdx.x);
   if (t_all < 0) return;
   const int e = find_entry(args.tm, t_all);
-  ns_tile<OP>(args.mats[args.tm.perm[e]], t_all - args.tm.start[e], args.src, args.first, args.a, args.b, args.c,
-              smem);
+  ns_tile_any<OP>(args.mats[args.tm.perm[e]], t_all - args.tm.start[e], args.src, args.first, args.a, args.b,
+                  args.c, smem);
 }
 
 // All Newton-Schulz iterations of a step in one launch. Each XCD serves its
@@ -620,11 +645,11 @@ __global__ __launch_bounds__(NTHR, 1) void ns_persistent_kernel(const MatDesc* _
     const MatDesc& d = mats[m];
     const int it = itop >> 2, op = itop & 3;
     if (op == OP_GRAM)
-      ns_tile<OP_GRAM>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
+      ns_tile_any<OP_GRAM>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
     else if (op == OP_SQUARE)
-      ns_tile<OP_SQUARE>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
+      ns_tile_any<OP_SQUARE>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
     else
-      ns_tile<OP_APPLY>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
+      ns_tile_any<OP_APPLY>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
     asm volatile("s_waitcnt vmcnt(0)" ::: "memory");   // this thread's stores are in L2
     __syncthreads();
     if (threadIdx.x == 0) __hip_atomic_fetch_add(q.count + 32 * m, 1, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);

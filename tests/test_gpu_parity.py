@@ -438,6 +438,26 @@ def test_two_steps_continue_from_state():
         assert rel(host(t.param), w["W64"]) < 1e-5
 
 
+def test_operand_layouts_same_bits():
+    """SQUARE and APPLY read their symmetric operand row-wise or k-major
+    (chosen by size); both readings see the same values, so the results are
+    the same bits, tall and ragged matrices included."""
+    flush("operand layouts")
+    xs = [randn((4, 768, 768), 81).to(torch.bfloat16), randn((3072, 768), 82).to(torch.bfloat16),
+          randn((300, 200), 83).to(torch.bfloat16), randn((2304, 2560), 84).to(torch.bfloat16)]
+    hp = ma.muon_hparams(ns_dtype="bf16")
+    outs = {}
+    for mode in ("rows", "kmajor"):
+        os.environ["MA_NS_OPERANDS"] = mode
+        try:
+            outs[mode] = [ma.newton_schulz(x.to(DEV), hp).cpu() for x in xs]
+        finally:
+            del os.environ["MA_NS_OPERANDS"]
+    for i in range(len(xs)):
+        assert torch.equal(outs["rows"][i].view(torch.int16), outs["kmajor"][i].view(torch.int16)), i
+    assert rel(host(outs["rows"][3]), omuon.newton_schulz(host(xs[3]))) < 2e-2
+
+
 def test_symmetric_products_stored_symmetric():
     """A = X X^T and B = bA + cA^2 hold equal values in both triangles, bit
     for bit (one triangle is computed and stored twice), so SQUARE and APPLY
