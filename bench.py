@@ -36,6 +36,8 @@ def parse():
     ap.add_argument("--cpu-budget", type=float, default=15.0, help="seconds of oracle work to time")
     ap.add_argument("--calib-copy", action="store_true",
                     help="also run a plain 1 GiB device copy (counter calibration)")
+    ap.add_argument("--no-next-rows", action="store_true",
+                    help="skip timing the global-norm pass and the AdamW variants")
     return ap.parse_args()
 
 
@@ -55,6 +57,46 @@ def ns_flops_per_launch(mats):
 def ns_flops_persistent(mats, steps):
     """Algorithmic FLOPs of the single launch that runs every iteration."""
     return sum(ns_flops(r, c, steps) for r, c in mats)
+
+
+def next_rows(data, aparams, ah, stream, reps):
+    """Kernel times of the rows after the hot path, outside the timed step:
+    the global-norm pass over every gradient of the step (one read of each),
+    and AdamW with bf16 moments (20 B per fp32 element) and with the cautious
+    wrapper (28 B). Runs on copies; the step's own state is untouched."""
+    import torch
+    import muon_adamw_amd as ma
+    out = {}
+    grads = [t.grad for t in data.muon if t.grad is not None] + [a.grad for a in aparams]
+    gbytes = sum(g.numel() * g.element_size() for g in grads)
+    state = torch.zeros(4, dtype=torch.float32, device=grads[0].device)
+    ma.global_grad_norm(grads, 1.0, state)
+    ma.profile_begin()
+    for _ in range(reps):
+        ma.global_grad_norm(grads, 1.0, state, stream=stream)
+    prof = ma.profile_end()
+    us = sum(v[1] for v in prof.values()) / reps * 1e3
+    out["global_grad_norm"] = {"avg_us": us, "bytes": gbytes, "achieved": gbytes / us / 1e3,
+                               "unit": "GB/s", "frac": gbytes / us / 1e3 / HBM_PEAK_GBPS,
+                               "kernels": {k: v[1] / reps * 1e3 for k, v in prof.items()}}
+    if aparams:
+        n = sum(a.param.numel() for a in aparams)
+        for name, kw, mdt, per in (("adamw_bf16_moments", {}, torch.bfloat16, 20),
+                                   ("adamw_cautious", {"cautious": True}, torch.float32, 28)):
+            cp = [ma.AdamWParam(a.param.clone(), a.grad, a.m.to(mdt), a.v.to(mdt), a.lr, a.weight_decay)
+                  for a in aparams]
+            ma.adamw_step(cp, ah.beta1, ah.beta2, ah.eps, ah.step, stream, **kw)
+            ma.profile_begin()
+            for i in range(reps):
+                ma.adamw_step(cp, ah.beta1, ah.beta2, ah.eps, ah.step + 1 + i, stream, **kw)
+            prof = ma.profile_end()
+            us = prof["adamw"][1] / prof["adamw"][0] * 1e3
+            by = n * per if all(a.param.dtype == torch.float32 for a in aparams) else None
+            out[name] = {"avg_us": us, "bytes": by, "achieved": None if by is None else by / us / 1e3,
+                         "unit": "GB/s", "frac": None if by is None else by / us / 1e3 / HBM_PEAK_GBPS}
+            del cp
+    torch.cuda.synchronize()
+    return out
 
 
 def elementwise_bytes(wl):
@@ -194,6 +236,8 @@ def main():
         torch.cuda.synchronize()
         del a, b
 
+    nxt = None if args.no_next_rows else next_rows(data, aparams, ah, stream, args.profile_steps)
+
     mats = [(min(m, n), max(m, n)) for (_, _, _, m, n) in wl.matrices()]
     fl = ns_flops_per_launch(mats)
     fl["ns_persistent_bf16"] = ns_flops_persistent(mats, h.ns_steps)
@@ -249,6 +293,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "cpu_baseline": cpu,
+        "next_rows": nxt,
     }
     print(json.dumps(line), flush=True)
 

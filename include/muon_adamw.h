@@ -114,6 +114,16 @@ typedef struct {
  *                  unit L2 norm with eps inside each square root (speedtronic
  *                  "Muon+"). normuon and muon_plus together: MA_E_UNSUPPORTED.
  * cautious         ma_cautious.
+ * ns_table         host array of ns_steps x 3 floats: iteration i uses
+ *                  (a, b, c) = row i (flaxchat "Muon Algorithm" step 2 loops
+ *                  over a list of coefficient triples); NULL uses (ns_a, ns_b,
+ *                  ns_c) at every iteration. Read during the call only.
+ * ns_norm_scale    X <- Q / (||Q||_F * ns_norm_scale + ns_eps); flaxchat's
+ *                  step 2 divides by ||g|| * 1.01. 0 reads as 1.
+ * clip             device, 16-byte aligned: the state ma_global_grad_norm
+ *                  wrote for this step, or NULL. The gradient is read times
+ *                  clip[1]; clip[2] != 0 skips the call's updates entirely
+ *                  (parameters, momentum and V bitwise unchanged).
  * After these, W <- (1 - lr*wd) W - lr * sqrt(max(1, m/n)) * U with m x n the
  * view's stored shape, subject to the cautious mask.
  */
@@ -133,6 +143,10 @@ typedef struct {
   int32_t muon_plus;
   int32_t cautious;
   int32_t pad_;
+  const float* ns_table;  /* host, ns_steps x 3, or NULL                      */
+  const float* clip;      /* device clip state, or NULL                       */
+  float ns_norm_scale;    /* 0 reads as 1                                      */
+  int32_t pad2_;
 } ma_muon_hparams;
 
 /* Device bytes of workspace muon_step needs for this tensor list (host call,
@@ -156,36 +170,91 @@ ma_status muon_step(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hpar
 /*
  * One tensor stepped by AdamW (dew.training.optim: optax.adamw; speedtronic
  * "v2 optimizers": torch AdamW). param (param_dtype), grad (grad_dtype), m and
- * v (fp32) are device arrays of `numel` elements; param, m, v are updated in
- * place. grad == NULL skips the tensor.
+ * v (moment_dtype) are device arrays of `numel` elements; param, m, v are
+ * updated in place. grad == NULL skips the tensor.
+ * moment_dtype MA_BF16 stores both moments in bf16 (dew.training.optim
+ * "bf16_moments"): they are widened to fp32 for the update and written back
+ * stochastically rounded ("stochastic_round_bf16": 16 uniform bits added below
+ * the kept mantissa, then truncated; NaN stays NaN). The bits are the top 16 of
+ * SplitMix64's output at state key + (i + 1) * 0x9E3779B97F4A7C15 for the
+ * element's flat index i, with key = mix(seed ^ mix((step << 32) + (tensor
+ * index << 1) + moment)), moment 0 for m and 1 for v, mix = SplitMix64's
+ * output function (Steele, Lea and Flood, OOPSLA 2014).
  */
 typedef struct {
   void* param;
   const void* grad;
-  float* m;
-  float* v;
+  void* m;
+  void* v;
   int64_t numel;
   int32_t param_dtype;
   int32_t grad_dtype;
   float lr;
   float weight_decay;
+  int32_t moment_dtype;  /* ma_dtype; 0 = fp32 */
+  int32_t pad_;
 } ma_adamw_tensor;
 
 /*
  * m <- beta1 m + (1-beta1) g; v <- beta2 v + (1-beta2) g^2;
  * p <- p - lr * ( (m/(1-beta1^step)) / (sqrt(v/(1-beta2^step)) + eps) + wd p ).
- * step >= 1 counts successful updates (the caller's host counter).
+ * step >= 1 counts successful updates (the caller's host counter; a step the
+ * clip state skipped is not one).
+ * cautious   MA_CAUTIOUS_WRAPPER (speedtronic "Cautious updates": "cautious
+ *            composes with either base optimizer") keeps an entry's observed
+ *            update, decay included, only where update * g > 0 and leaves the
+ *            parameter as it was elsewhere; m and v are updated either way.
+ *            MA_CAUTIOUS_WD_MASK is Muon's rule: MA_E_UNSUPPORTED.
+ * seed       stochastic-rounding seed of bf16 moments.
+ * clip       as in ma_muon_hparams: g is read times clip[1], clip[2] != 0
+ *            skips every update of the call.
  */
 typedef struct {
   double beta1;
   double beta2;
   double eps;
   int64_t step;
+  int32_t cautious;      /* MA_CAUTIOUS_NONE or MA_CAUTIOUS_WRAPPER */
+  int32_t pad_;
+  uint64_t seed;
+  const float* clip;     /* device clip state, or NULL */
 } ma_adamw_hparams;
 
 /* The AdamW half of the hybrid step over `n` tensors; no workspace. */
 ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_hparams* hp,
                      void* stream);
+
+/*
+ * Global gradient norm over every gradient of the hybrid step (dew.training.
+ * optim "build_optimizer": the global-norm clip reads every gradient
+ * together, before the parameter groups split them; kimi-k3 "Optimization":
+ * with max_grad_norm > 0 the norm is clipped, with 0 it is only observed, and
+ * an overflow skips the whole hybrid update).
+ *
+ * grads      host array of n gradient references (device arrays; grad NULL
+ *            or numel 0 contributes nothing). Pass the Muon and the AdamW
+ *            gradients of the step together.
+ * state      device, 4 floats, 16-byte aligned, written on the stream:
+ *            [0] ||g||_2 over all elements (fp32 partial sums per 8192
+ *            elements, added in fp64 in a fixed order: the same bits for the
+ *            same inputs), [1] the clip factor min(1, max_norm / ||g||) (1 when
+ *            max_norm <= 0 or ||g|| <= max_norm), [2] 1 when ||g|| is not
+ *            finite (the step is to be skipped), else 0, [3] 0.
+ *            Hand `state` to muon_step and adamw_step (hparams.clip): they read
+ *            it on the device, so nothing waits for the host. A caller that
+ *            counts successful steps reads [2] back after the step.
+ * workspace  device, ma_grad_norm_workspace_bytes() bytes, 256-byte aligned.
+ */
+typedef struct {
+  const void* grad;
+  int64_t numel;
+  int32_t dtype;         /* ma_dtype */
+  int32_t pad_;
+} ma_grad_ref;
+
+size_t ma_grad_norm_workspace_bytes(const ma_grad_ref* grads, int32_t n);
+ma_status ma_global_grad_norm(const ma_grad_ref* grads, int32_t n, float max_norm, float* state,
+                              void* workspace, size_t workspace_bytes, void* stream);
 
 /* Thread-local message for the last non-OK status of this thread. */
 const char* ma_last_error(void);

@@ -41,19 +41,26 @@ class MuonHParamsC(ctypes.Structure):
                 ("nesterov", ctypes.c_int32), ("ns_steps", ctypes.c_int32),
                 ("ns_dtype", ctypes.c_int32), ("normuon", ctypes.c_int32),
                 ("muon_plus", ctypes.c_int32), ("cautious", ctypes.c_int32),
-                ("pad_", ctypes.c_int32)]
+                ("pad_", ctypes.c_int32), ("ns_table", ctypes.POINTER(ctypes.c_float)),
+                ("clip", ctypes.c_void_p), ("ns_norm_scale", ctypes.c_float), ("pad2_", ctypes.c_int32)]
 
 
 class AdamWTensorC(ctypes.Structure):
     _fields_ = [("param", ctypes.c_void_p), ("grad", ctypes.c_void_p), ("m", ctypes.c_void_p),
                 ("v", ctypes.c_void_p), ("numel", ctypes.c_int64), ("param_dtype", ctypes.c_int32),
                 ("grad_dtype", ctypes.c_int32), ("lr", ctypes.c_float),
-                ("weight_decay", ctypes.c_float)]
+                ("weight_decay", ctypes.c_float), ("moment_dtype", ctypes.c_int32), ("pad_", ctypes.c_int32)]
 
 
 class AdamWHParamsC(ctypes.Structure):
     _fields_ = [("beta1", ctypes.c_double), ("beta2", ctypes.c_double), ("eps", ctypes.c_double),
-                ("step", ctypes.c_int64)]
+                ("step", ctypes.c_int64), ("cautious", ctypes.c_int32), ("pad_", ctypes.c_int32),
+                ("seed", ctypes.c_uint64), ("clip", ctypes.c_void_p)]
+
+
+class GradRefC(ctypes.Structure):
+    _fields_ = [("grad", ctypes.c_void_p), ("numel", ctypes.c_int64), ("dtype", ctypes.c_int32),
+                ("pad_", ctypes.c_int32)]
 
 
 class MatrixInfoC(ctypes.Structure):
@@ -71,7 +78,8 @@ class KernelTimeC(ctypes.Structure):
 
 EXPORTS = ("muon_step", "adamw_step", "ma_muon_workspace_bytes", "ma_last_error",
            "ma_newton_schulz", "ma_newton_schulz_workspace_bytes", "ma_muon_plan_counts",
-           "ma_muon_matrix_info", "ma_profile_begin", "ma_profile_end")
+           "ma_muon_matrix_info", "ma_profile_begin", "ma_profile_end", "ma_grad_norm_workspace_bytes",
+           "ma_global_grad_norm")
 
 _lib = None
 
@@ -107,6 +115,10 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_profile_begin.restype = ctypes.c_int
     lib.ma_profile_end.argtypes = [ctypes.POINTER(KernelTimeC), I32]
     lib.ma_profile_end.restype = I32
+    lib.ma_grad_norm_workspace_bytes.argtypes = [ctypes.POINTER(GradRefC), I32]
+    lib.ma_grad_norm_workspace_bytes.restype = SZ
+    lib.ma_global_grad_norm.argtypes = [ctypes.POINTER(GradRefC), I32, ctypes.c_float, P, P, SZ, P]
+    lib.ma_global_grad_norm.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -167,9 +179,16 @@ class AdamWParam:
     weight_decay: float = 0.1
 
 
+def _ptr(t) -> Optional[int]:
+    return None if t is None else (t if isinstance(t, int) else t.data_ptr())
+
+
 def muon_hparams(beta=0.95, nesterov=True, ns_steps=5, ns_coeffs=NS_COEFFS, ns_eps=1e-7,
                  ns_dtype="bf16", normuon=False, normuon_beta2=0.95, muon_plus=False,
-                 muon_plus_eps=1e-8, cautious="none") -> MuonHParamsC:
+                 muon_plus_eps=1e-8, cautious="none", ns_table=None, ns_norm_scale=1.0,
+                 clip=None) -> MuonHParamsC:
+    """``ns_table``: one (a, b, c) per iteration (ns_steps rows), or None.
+    ``clip``: the device state tensor global_grad_norm wrote, or None."""
     a, b, c = ns_coeffs
     h = MuonHParamsC()
     h.beta, h.normuon_beta2 = beta, normuon_beta2
@@ -177,6 +196,15 @@ def muon_hparams(beta=0.95, nesterov=True, ns_steps=5, ns_coeffs=NS_COEFFS, ns_e
     h.nesterov, h.ns_steps = int(bool(nesterov)), int(ns_steps)
     h.ns_dtype = MA_BF16 if ns_dtype == "bf16" else MA_F32
     h.normuon, h.muon_plus, h.cautious = int(bool(normuon)), int(bool(muon_plus)), CAUTIOUS[cautious]
+    if ns_table is not None:
+        rows = [tuple(r) for r in ns_table]
+        if len(rows) != ns_steps or any(len(r) != 3 for r in rows):
+            raise ValueError("ns_table needs one (a, b, c) row per Newton-Schulz step")
+        arr = (ctypes.c_float * (3 * ns_steps))(*[float(x) for r in rows for x in r])
+        h._table = arr   # keeps the host array alive as long as the struct
+        h.ns_table = ctypes.cast(arr, ctypes.POINTER(ctypes.c_float))
+    h.ns_norm_scale = ns_norm_scale
+    h.clip = _ptr(clip)
     return h
 
 
@@ -249,7 +277,11 @@ def muon_step(tensors: Sequence[MuonParam], hp: MuonHParamsC, workspace: Optiona
     return workspace
 
 
-def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, step=1, stream=None):
+def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, step=1, stream=None,
+               cautious=False, seed=0, clip=None):
+    """The AdamW half. m and v are float32 or bfloat16 (stochastic rounding,
+    seeded by ``seed``, the step, the tensor and the moment); ``cautious``:
+    the wrapper mask; ``clip``: the device state global_grad_norm wrote."""
     lib = load_library()
     arr = (AdamWTensorC * max(len(tensors), 1))()
     device = None
@@ -260,10 +292,11 @@ def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, s
             raise ValueError(f"adamw[{i}].param must be on a GPU")
         device = device or t.param.device
         n = t.param.numel()
-        if t.m.dtype != torch.float32 or t.v.dtype != torch.float32 or t.m.numel() != n or t.v.numel() != n:
-            raise ValueError(f"adamw[{i}]: m and v must be float32 with param's numel")
+        if t.m.dtype != t.v.dtype or t.m.numel() != n or t.v.numel() != n:
+            raise ValueError(f"adamw[{i}]: m and v must share a dtype and have param's numel")
         d = arr[i]
         d.param, d.m, d.v, d.numel = t.param.data_ptr(), t.m.data_ptr(), t.v.data_ptr(), n
+        d.moment_dtype = _dtype_code(t.m)
         d.param_dtype = _dtype_code(t.param)
         if t.grad is not None:
             _check_dense(t.grad, f"adamw[{i}].grad")
@@ -274,8 +307,41 @@ def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, s
             d.grad, d.grad_dtype = None, d.param_dtype
         d.lr, d.weight_decay = t.lr, t.weight_decay
     hp = AdamWHParamsC(beta1, beta2, eps, int(step))
+    hp.cautious = CAUTIOUS["wrapper"] if cautious else 0
+    hp.seed = int(seed) & ((1 << 64) - 1)
+    hp.clip = _ptr(clip)
     _check(lib.adamw_step(arr, len(tensors), ctypes.byref(hp),
                           ctypes.c_void_p(_stream_handle(stream, device or torch.device("cuda")))))
+
+
+def global_grad_norm(grads: Sequence[Optional[torch.Tensor]], max_norm: float = 0.0,
+                     state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+                     stream=None) -> torch.Tensor:
+    """Global gradient norm and clip state over ``grads`` (None entries skip).
+    Returns the device state: [norm, clip factor, skip flag, 0]."""
+    lib = load_library()
+    arr = (GradRefC * max(len(grads), 1))()
+    device = None
+    for i, g in enumerate(grads):
+        if g is None:
+            continue
+        _check_dense(g, f"grads[{i}]")
+        if not g.is_cuda:
+            raise ValueError(f"grads[{i}] must be on a GPU")
+        device = device or g.device
+        arr[i].grad, arr[i].numel, arr[i].dtype = g.data_ptr(), g.numel(), _dtype_code(g)
+    device = device or torch.device("cuda")
+    if state is None:
+        state = torch.empty(4, dtype=torch.float32, device=device)
+    need = lib.ma_grad_norm_workspace_bytes(arr, len(grads))
+    if need == 0:
+        raise MuonAdamWError(1, lib.ma_last_error().decode())
+    if workspace is None or workspace.numel() < need:
+        workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _check(lib.ma_global_grad_norm(arr, len(grads), float(max_norm), ctypes.c_void_p(state.data_ptr()),
+                                   ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
+                                   ctypes.c_void_p(_stream_handle(stream, device))))
+    return state
 
 
 def newton_schulz(x: torch.Tensor, hp: Optional[MuonHParamsC] = None, out: Optional[torch.Tensor] = None,

@@ -70,6 +70,7 @@ struct Plan {
   // persistent Newton-Schulz launch (bf16): per-XCD segment lists in `ints`
   // (int4 records from byte segs_off) and a zeroed counter region
   bool persist = false;
+  size_t coefs_off = 0;   // byte offset of the coefficient table within the int tables
   int operands = 0;   // 0: by size (k-major up to kKmajorMaxRows), 1: k-major, 2: row-wise
   size_t segs_off = 0, off_counters = 0;
   int counter_ints = 0;
@@ -162,8 +163,21 @@ ma_status validate_hparams(const ma_muon_hparams* hp) {
     return fail(MA_E_INVALID, "muon_plus_eps must be finite and >= 0");
   if (hp->cautious < MA_CAUTIOUS_NONE || hp->cautious > MA_CAUTIOUS_WRAPPER)
     return fail(MA_E_INVALID, "cautious must be 0 (none), 1 (weight-decay mask) or 2 (wrapper)");
+  if (hp->ns_table)
+    for (int i = 0; i < 3 * hp->ns_steps; ++i)
+      if (!std::isfinite(hp->ns_table[i])) return fail(MA_E_INVALID, "ns_table entries must be finite");
+  if (!(hp->ns_norm_scale >= 0.f) || !std::isfinite(hp->ns_norm_scale))
+    return fail(MA_E_INVALID, "ns_norm_scale must be finite and >= 0 (0 reads as 1)");
+  if (reinterpret_cast<uintptr_t>(hp->clip) % 16) return fail(MA_E_INVALID, "clip state must be 16-byte aligned");
   return MA_OK;
 }
+
+// Coefficient k (0: a, 1: b, 2: c) of Newton-Schulz iteration `it`.
+float ns_coef(const ma_muon_hparams* hp, int it, int k) {
+  if (hp->ns_table) return hp->ns_table[3 * it + k];
+  return k == 0 ? hp->ns_a : (k == 1 ? hp->ns_b : hp->ns_c);
+}
+float ns_norm_scale(const ma_muon_hparams* hp) { return hp->ns_norm_scale > 0.f ? hp->ns_norm_scale : 1.0f; }
 
 struct Range {
   uintptr_t lo, hi;
@@ -358,6 +372,15 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
   P.rows_t = add_map(P, rows_t);
   P.cols_nt = add_map(P, cols_nt);
   P.out = add_map(P, out);
+  // the (a, b, c) of every iteration, as float bits
+  P.coefs_off = P.ints.size() * sizeof(int32_t);
+  for (int it = 0; it < hp->ns_steps; ++it)
+    for (int k = 0; k < 3; ++k) {
+      const float f = ns_coef(hp, it, k);
+      int32_t bits;
+      std::memcpy(&bits, &f, 4);
+      P.ints.push_back(bits);
+    }
 
   // Workspace layout: [MatDesc x nm][int tables] then per-matrix buffers.
   P.desc_bytes = align_up(sizeof(MatDesc) * std::max(nm, 1));
@@ -520,6 +543,7 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
     d.rfac = reinterpret_cast<float*>(base + mp.off_rf);
     d.cfac = reinterpret_cast<float*>(base + mp.off_cf);
     d.ntile_ew = mp.ntile_ew;
+    d.clip = ns_only ? nullptr : hp->clip;
     d.kmajor = P.operands == 1 || (P.operands == 0 && mp.rp <= kKmajorMaxRows);
   }
   std::memcpy(host.data() + P.desc_bytes, P.ints.data(), P.ints.size() * sizeof(int32_t));
@@ -533,7 +557,8 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
   (void)hipGetLastError();
   const int ew_dt = P.ns_dt;
   timed("momentum", s, [&] { launch_momentum(mats, TM(P.ew), ew_dt, beta, omb, hp->nesterov, s); });
-  timed("norm_finalize", s, [&] { launch_norm_finalize(mats, TM(P.fin_all), hp->ns_eps, s); });
+  timed("norm_finalize", s,
+        [&] { launch_norm_finalize(mats, TM(P.fin_all), hp->ns_eps, ns_norm_scale(hp), s); });
   static const char* const kNsNames[2][3] = {{"ns_gram_f32", "ns_square_f32", "ns_apply_f32"},
                                              {"ns_gram_bf16", "ns_square_bf16", "ns_apply_bf16"}};
   const int bf = P.ns_dt == MA_BF16;
@@ -547,17 +572,19 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
       q.seg_off[x] = P.seg_off[x];
       q.nseg[x] = P.nseg[x];
     }
-    timed("ns_persistent_bf16", s,
-          [&] { launch_ns_persistent(mats, q, P.counter_ints, hp->ns_a, hp->ns_b, hp->ns_c, s); });
+    q.coefs = reinterpret_cast<const float*>(base + P.desc_bytes + P.coefs_off);
+    q.clip = ns_only ? nullptr : hp->clip;
+    timed("ns_persistent_bf16", s, [&] { launch_ns_persistent(mats, q, P.counter_ints, s); });
   }
   for (int it = 0; it < (P.persist ? 0 : hp->ns_steps); ++it) {
     for (int op = NS_GRAM; op <= NS_APPLY; ++op) {
       const TileMap tm = TM(op == NS_APPLY ? P.app : (op == NS_GRAM ? P.gram : P.sq));
       timed(kNsNames[bf][op], s, [&] {
+        const float a = ns_coef(hp, it, 0), b = ns_coef(hp, it, 1), c = ns_coef(hp, it, 2);
         if (bf)
-          launch_ns_bf16(op, mats, tm, it & 1, it == 0, hp->ns_a, hp->ns_b, hp->ns_c, s);
+          launch_ns_bf16(op, mats, tm, it & 1, it == 0, a, b, c, s);
         else
-          launch_ns_f32(op, mats, tm, it & 1, it == 0, hp->ns_a, hp->ns_b, hp->ns_c, s);
+          launch_ns_f32(op, mats, tm, it & 1, it == 0, a, b, c, s);
       });
     }
   }
@@ -616,6 +643,7 @@ ma_muon_hparams ns_hparams(const ma_muon_hparams* hp) {
   h.normuon = 0;
   h.muon_plus = 0;
   h.cautious = 0;
+  h.clip = nullptr;
   return h;
 }
 
@@ -755,6 +783,83 @@ int32_t ma_profile_end(ma_kernel_time* out, int32_t max) {
   return w;
 }
 
+namespace {
+// Blocks of the grad-norm pass for one gradient reference.
+int64_t grad_norm_blocks(const ma_grad_ref& g) {
+  if (!g.grad || g.numel <= 0) return 0;
+  return (g.numel + kGradNormChunk - 1) / kGradNormChunk;
+}
+ma_status validate_grads(const ma_grad_ref* grads, int32_t n, int64_t& blocks) {
+  blocks = 0;
+  if (n < 0) return fail(MA_E_INVALID, "gradient count is negative");
+  if (n > 0 && !grads) return fail(MA_E_INVALID, "gradient array is NULL");
+  for (int i = 0; i < n; ++i) {
+    const ma_grad_ref& g = grads[i];
+    const std::string who = "gradient " + std::to_string(i) + ": ";
+    if (!dtype_ok(g.dtype)) return fail(MA_E_DTYPE, who + "dtype must be MA_F32 or MA_BF16");
+    if (g.numel < 0) return fail(MA_E_INVALID, who + "numel is negative");
+    if (g.grad && reinterpret_cast<uintptr_t>(g.grad) % dtype_size(g.dtype))
+      return fail(MA_E_INVALID, who + "not aligned to its element size");
+    blocks += grad_norm_blocks(g);
+  }
+  if (blocks > (int64_t(1) << 30)) return fail(MA_E_UNSUPPORTED, "too many gradient elements");
+  return MA_OK;
+}
+}  // namespace
+
+size_t ma_grad_norm_workspace_bytes(const ma_grad_ref* grads, int32_t n) {
+  int64_t blocks = 0;
+  if (validate_grads(grads, n, blocks) != MA_OK) return 0;
+  return align_up(static_cast<size_t>(std::max<int64_t>(blocks, 1)) * sizeof(float));
+}
+
+ma_status ma_global_grad_norm(const ma_grad_ref* grads, int32_t n, float max_norm, float* state, void* workspace,
+                              size_t workspace_bytes, void* stream) {
+  int64_t blocks = 0;
+  ma_status st = validate_grads(grads, n, blocks);
+  if (st != MA_OK) return st;
+  if (!std::isfinite(max_norm)) return fail(MA_E_INVALID, "max_norm must be finite");
+  if (!state || reinterpret_cast<uintptr_t>(state) % 16) return fail(MA_E_INVALID, "state must be a 16-byte aligned device pointer");
+  const size_t need = align_up(static_cast<size_t>(std::max<int64_t>(blocks, 1)) * sizeof(float));
+  if (!workspace) return fail(MA_E_WORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(MA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  if (workspace_bytes < need)
+    return fail(MA_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " + std::to_string(need));
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  (void)hipGetLastError();
+  float* partial = static_cast<float*>(workspace);
+  GradNormLaunch L{};
+  L.partial = partial;
+  int64_t done_blocks = 0, blocks_here = 0;
+  auto flush = [&]() {
+    if (L.nt == 0) return;
+    L.block_start[L.nt] = static_cast<int32_t>(blocks_here);
+    L.partial_off = static_cast<int32_t>(done_blocks);
+    timed("grad_sumsq", s, [&] { launch_grad_sumsq(L, static_cast<int>(blocks_here), s); });
+    done_blocks += blocks_here;
+    blocks_here = 0;
+    L.nt = 0;
+  };
+  for (int i = 0; i < n; ++i) {
+    const int64_t nb = grad_norm_blocks(grads[i]);
+    if (nb == 0) continue;
+    GradNormArg& a = L.t[L.nt];
+    a.g = grads[i].grad;
+    a.numel = grads[i].numel;
+    a.dt = grads[i].dtype;
+    L.block_start[L.nt] = static_cast<int32_t>(blocks_here);
+    blocks_here += nb;
+    ++L.nt;
+    if (L.nt == kMaxGradNormTensors) flush();
+  }
+  flush();
+  timed("grad_norm_finalize", s,
+        [&] { launch_grad_norm_finalize(partial, static_cast<int>(done_blocks), max_norm, state, s); });
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(MA_E_HIP, std::string("kernel launch failed: ") + hipGetErrorString(e));
+  return MA_OK;
+}
+
 ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_hparams* hp, void* stream) {
   if (!hp) return fail(MA_E_INVALID, "hparams is NULL");
   if (n < 0) return fail(MA_E_INVALID, "tensor count is negative");
@@ -763,12 +868,17 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
     return fail(MA_E_INVALID, "betas must be in [0, 1)");
   if (!(hp->eps >= 0.0) || !std::isfinite(hp->eps)) return fail(MA_E_INVALID, "eps must be finite and >= 0");
   if (hp->step < 1) return fail(MA_E_INVALID, "step must be >= 1");
+  if (hp->cautious == MA_CAUTIOUS_WD_MASK)
+    return fail(MA_E_UNSUPPORTED, "the weight-decay mask is Muon's rule; AdamW takes none or the wrapper");
+  if (hp->cautious != MA_CAUTIOUS_NONE && hp->cautious != MA_CAUTIOUS_WRAPPER)
+    return fail(MA_E_INVALID, "cautious must be 0 (none) or 2 (wrapper)");
+  if (reinterpret_cast<uintptr_t>(hp->clip) % 16) return fail(MA_E_INVALID, "clip state must be 16-byte aligned");
   std::vector<Range> ranges;
   for (int i = 0; i < n; ++i) {
     const ma_adamw_tensor& x = tensors[i];
     const std::string who = "tensor " + std::to_string(i) + ": ";
-    if (!dtype_ok(x.param_dtype) || !dtype_ok(x.grad_dtype))
-      return fail(MA_E_DTYPE, who + "param/grad dtype must be MA_F32 or MA_BF16 (complex is not supported)");
+    if (!dtype_ok(x.param_dtype) || !dtype_ok(x.grad_dtype) || !dtype_ok(x.moment_dtype))
+      return fail(MA_E_DTYPE, who + "param/grad/moment dtype must be MA_F32 or MA_BF16 (complex is not supported)");
     if (x.numel < 0) return fail(MA_E_INVALID, who + "numel is negative");
     if (!std::isfinite(x.lr) || !std::isfinite(x.weight_decay))
       return fail(MA_E_INVALID, who + "lr and weight_decay must be finite");
@@ -777,13 +887,14 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
     if (x.numel > (int64_t(1) << 40)) return fail(MA_E_UNSUPPORTED, who + "tensor too large");
     const uintptr_t pb = reinterpret_cast<uintptr_t>(x.param), mb = reinterpret_cast<uintptr_t>(x.m),
                     vb = reinterpret_cast<uintptr_t>(x.v);
-    if (pb % dtype_size(x.param_dtype) || mb % 4 || vb % 4 ||
+    const size_t mes = dtype_size(x.moment_dtype);
+    if (pb % dtype_size(x.param_dtype) || mb % mes || vb % mes ||
         reinterpret_cast<uintptr_t>(x.grad) % dtype_size(x.grad_dtype))
       return fail(MA_E_INVALID, who + "buffers not aligned to their element size");
     const uintptr_t ne = static_cast<uintptr_t>(x.numel);
     ranges.push_back({pb, pb + ne * dtype_size(x.param_dtype), i, "param"});
-    ranges.push_back({mb, mb + ne * 4, i, "m"});
-    ranges.push_back({vb, vb + ne * 4, i, "v"});
+    ranges.push_back({mb, mb + ne * mes, i, "m"});
+    ranges.push_back({vb, vb + ne * mes, i, "v"});
   }
   ma_status st = check_overlaps(ranges);
   if (st != MA_OK) return st;
@@ -798,6 +909,15 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
   L.eps = static_cast<float>(hp->eps);
   L.inv_bc1 = static_cast<float>(1.0 / (1.0 - std::pow(b1, static_cast<double>(hp->step))));
   L.inv_sqrt_bc2 = static_cast<float>(1.0 / std::sqrt(1.0 - std::pow(b2, static_cast<double>(hp->step))));
+  L.cautious = hp->cautious == MA_CAUTIOUS_WRAPPER;
+  L.clip = hp->clip;
+  // stochastic-rounding key of (tensor, moment): SplitMix64's output of the
+  // seed mixed with (step, tensor, moment)
+  auto sr_key = [&](int leaf, int moment) {
+    const uint64_t c = (static_cast<uint64_t>(hp->step) << 32) + (static_cast<uint64_t>(leaf) << 1) +
+                       static_cast<uint64_t>(moment);
+    return splitmix64_mix(hp->seed ^ splitmix64_mix(c));
+  };
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
   int64_t blocks = 0;
@@ -818,13 +938,18 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
       const int64_t room = (int64_t(1) << 30) - blocks;
       const int64_t take = std::min(nb, room);
       AdamTensorArg& a = L.t[L.nt];
+      const size_t mes = dtype_size(x.moment_dtype);
       a.p = static_cast<char*>(x.param) + done * kAdamChunk * dtype_size(x.param_dtype);
       a.g = static_cast<const char*>(x.grad) + done * kAdamChunk * dtype_size(x.grad_dtype);
-      a.m = x.m + done * kAdamChunk;
-      a.v = x.v + done * kAdamChunk;
+      a.m = static_cast<char*>(x.m) + done * kAdamChunk * mes;
+      a.v = static_cast<char*>(x.v) + done * kAdamChunk * mes;
       a.numel = std::min(x.numel - done * kAdamChunk, take * kAdamChunk);
+      a.index0 = done * kAdamChunk;
+      a.key_m = sr_key(i, 0);
+      a.key_v = sr_key(i, 1);
       a.pdt = x.param_dtype;
       a.gdt = x.grad_dtype;
+      a.mdt = x.moment_dtype;
       a.lr = x.lr;
       a.wd = x.weight_decay;
       L.block_start[L.nt] = static_cast<int32_t>(blocks);

@@ -50,9 +50,13 @@ struct MatDesc {
   float* csum_c;      // canonical column sums of squares, cp entries
   float* rfac;        // per stored row factor, m entries
   float* cfac;        // per stored column factor, n entries
+  // global-norm clip state of the step (ma_global_grad_norm: [1] the factor
+  // the gradient is read with, [2] nonzero: skip every update), or null
+  const float* clip;
   int32_t ntile_ew;   // number of momentum-pass tiles (= partial count)
   int32_t kmajor;     // SQUARE and APPLY read both operands k-major (else row-wise)
 };
+
 
 // Maps a flat block index to (matrix, local tile) for one launch: matrices
 // are visited in `perm` order; entry k owns tiles [start[k], start[k+1]).
@@ -85,6 +89,8 @@ struct NsQueue {
   int* qhead;
   int* err;
   int* count;
+  const float* coefs;   // (a, b, c) of each iteration, 3 floats per iteration
+  const float* clip;    // the step's clip state or null: a skipped step runs no tile
   int32_t seg_off[8];
   int32_t nseg[8];
 };
@@ -145,6 +151,14 @@ __device__ __forceinline__ float wave_sum(float v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;
+}
+
+// The step is skipped (clip state says so): nothing may be written.
+__device__ __forceinline__ bool step_skipped(const float* clip) {
+  return clip != nullptr && __builtin_amdgcn_readfirstlane(__float_as_uint(gmem(clip)[2])) != 0u;
+}
+__device__ __forceinline__ float clip_factor(const float* clip) {
+  return clip != nullptr ? __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(gmem(clip)[1]))) : 1.0f;
 }
 
 }  // namespace ma

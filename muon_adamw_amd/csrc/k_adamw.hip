@@ -2,96 +2,151 @@
 // OPTIMIZER_MAP; speedtronic "v2 optimizers" page: torch AdamW):
 //   m <- b1 m + (1-b1) g;  v <- b2 v + (1-b2) g^2
 //   p <- p - lr ( (m / (1-b1^t)) / (sqrt(v / (1-b2^t)) + eps) + wd p )
-// Pure HBM streaming: 28 B per fp32 element (read p, g, m, v; write p, m, v).
-// Up to 32 tensors per launch travel in the kernel arguments; each block owns
-// one contiguous chunk of one tensor. A full chunk of fp32 tensors (the common
-// case) is exactly two 16-byte slots per stream per thread: all eight loads
-// are issued before any use, and every access is nontemporal, since nothing
-// here is read again within the step (measured on MI355X: 74% of HBM peak
-// against 64% with cached accesses; the stores are what matters).
-// IEEE sqrt and division (no approximate reciprocal square root).
+// with, per launch:
+//   * the global-norm clip (kimi-k3 "Optimization": the trainer clips the
+//     global gradient norm before either optimizer; an overflow skips the
+//     whole hybrid update): g is read times the clip factor, and a skipped
+//     step writes nothing;
+//   * the cautious wrapper (speedtronic "Cautious updates"; "cautious
+//     composes with either base optimizer"): an entry keeps its observed
+//     update, decay included, only where update * g > 0, else p is left as
+//     it was; m and v are always the base optimizer's;
+//   * bf16 moments (dew.training.optim "bf16_moments"): m and v are read,
+//     widened to fp32, updated, and written back stochastically rounded
+//     ("stochastic_round_bf16": 16 uniform bits added below the kept
+//     mantissa, then truncated; NaN stays NaN). The 16 bits are the top of
+//     SplitMix64's output at state key + (index + 1) * gamma, with index the
+//     element's flat position in its tensor and key derived on the host from
+//     the seed, the step, the tensor and the moment.
+// Pure HBM streaming: 28 B per fp32 element (read p, g, m, v; write p, m, v),
+// 20 B with bf16 moments. Each block owns one contiguous chunk of one tensor.
+// A full chunk of fp32 parameters and gradients (the common case) is two
+// 16-byte slots per stream per thread: all loads are issued before any use,
+// and every access is nontemporal, since nothing here is read again within
+// the step (measured on MI355X: 74% of HBM peak against 64% with cached
+// accesses; the stores are what matters). IEEE sqrt and division.
 #include "kernels.hpp"
 
 namespace ma {
 
 namespace {
 
-__device__ __forceinline__ void adam_elem(float& p, float g, float& m, float& v, const AdamLaunch& L,
-                                          float lr, float wd) {
+typedef __attribute__((address_space(1))) gf4 ggf4;
+typedef __attribute__((address_space(1))) gu2 ggu2;
+
+__device__ __forceinline__ float adam_elem(float p, float g, float& m, float& v, const AdamLaunch& L, float lr,
+                                           float wd) {
   m = L.b1 * m + L.omb1 * g;
   v = L.b2 * v + L.omb2 * (g * g);
   const float denom = sqrtf(v) * L.inv_sqrt_bc2 + L.eps;
-  p = p - lr * ((m * L.inv_bc1) / denom + wd * p);
+  const float pn = p - lr * ((m * L.inv_bc1) / denom + wd * p);
+  // the observed update p - pn is kept only where it points along g
+  return (L.cautious && !((p - pn) * g > 0.f)) ? p : pn;
+}
+
+// Stochastic rounding of x to bf16 bits with the counter hash.
+__device__ __forceinline__ uint32_t sr_bf16(float x, uint64_t key, int64_t index) {
+  const uint32_t u = __float_as_uint(x);
+  if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;   // NaN stays a (quiet) NaN
+  const uint32_t r = static_cast<uint32_t>(splitmix64_mix(key + static_cast<uint64_t>(index + 1) * kSplitMixGamma) >> 48);
+  return (u + r) >> 16;
+}
+__device__ __forceinline__ gu2 sr_bf16x4(const gf4& x, uint64_t key, int64_t index) {
+  gu2 o;
+  o.x = sr_bf16(x.x, key, index) | (sr_bf16(x.y, key, index + 1) << 16);
+  o.y = sr_bf16(x.z, key, index + 2) | (sr_bf16(x.w, key, index + 3) << 16);
+  return o;
+}
+__device__ __forceinline__ gf4 widen4(const gu2& b) {
+  return gf4{__uint_as_float(b.x << 16), __uint_as_float(b.x & 0xffff0000u), __uint_as_float(b.y << 16),
+             __uint_as_float(b.y & 0xffff0000u)};
 }
 
 __global__ __launch_bounds__(256) void adamw_kernel(const AdamLaunch L) {
+  if (step_skipped(L.clip)) return;
+  const float cf = clip_factor(L.clip);
   int ti = 0;
   while (ti + 1 < L.nt && L.block_start[ti + 1] <= static_cast<int>(blockIdx.x)) ++ti;
   const AdamTensorArg& T = L.t[ti];
   const int64_t c0 = (int64_t)(blockIdx.x - L.block_start[ti]) * kAdamChunk;
   const int64_t c1 = c0 + kAdamChunk < T.numel ? c0 + kAdamChunk : T.numel;
   const float lr = T.lr, wd = T.wd;
-  const bool vec = T.pdt == DT_F32 && T.gdt == DT_F32 &&
-                   ((reinterpret_cast<uintptr_t>(T.p) | reinterpret_cast<uintptr_t>(T.g) |
-                     reinterpret_cast<uintptr_t>(T.m) | reinterpret_cast<uintptr_t>(T.v)) & 15) == 0;
-  if (vec && c1 - c0 == kAdamChunk) {
-    static_assert(kAdamChunk == 2 * 256 * 4, "a full chunk is two float4 slots per thread");
-    typedef __attribute__((address_space(1))) gf4 ggf4;
+  const bool bfm = T.mdt == DT_BF16;
+  const uintptr_t al = reinterpret_cast<uintptr_t>(T.p) | reinterpret_cast<uintptr_t>(T.g) |
+                       reinterpret_cast<uintptr_t>(T.m) | reinterpret_cast<uintptr_t>(T.v);
+  const bool full = T.pdt == DT_F32 && T.gdt == DT_F32 && (al & 15) == 0 && c1 - c0 == kAdamChunk;
+  if (full) {
+    static_assert(kAdamChunk == 2 * 256 * 4, "a full chunk is two 4-element slots per thread");
     ggf4* P4 = reinterpret_cast<ggf4*>(gmem(static_cast<float*>(T.p) + c0));
     const ggf4* G4 = reinterpret_cast<const ggf4*>(gmem(static_cast<const float*>(T.g) + c0));
-    ggf4* M4 = reinterpret_cast<ggf4*>(gmem(T.m + c0));
-    ggf4* V4 = reinterpret_cast<ggf4*>(gmem(T.v + c0));
     gf4 p[2], g[2], m[2], v[2];
+    if (!bfm) {
+      ggf4* M4 = reinterpret_cast<ggf4*>(gmem(static_cast<float*>(T.m) + c0));
+      ggf4* V4 = reinterpret_cast<ggf4*>(gmem(static_cast<float*>(T.v) + c0));
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = threadIdx.x + 256 * u;
-      p[u] = __builtin_nontemporal_load(P4 + i);
-      g[u] = __builtin_nontemporal_load(G4 + i);
-      m[u] = __builtin_nontemporal_load(M4 + i);
-      v[u] = __builtin_nontemporal_load(V4 + i);
-    }
-#pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int i = threadIdx.x + 256 * u;
-#pragma unroll
-      for (int k = 0; k < 4; ++k) {
-        float pk = p[u][k], mk = m[u][k], vk = v[u][k];
-        adam_elem(pk, g[u][k], mk, vk, L, lr, wd);
-        p[u][k] = pk; m[u][k] = mk; v[u][k] = vk;
+      for (int u = 0; u < 2; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        p[u] = __builtin_nontemporal_load(P4 + i);
+        g[u] = __builtin_nontemporal_load(G4 + i);
+        m[u] = __builtin_nontemporal_load(M4 + i);
+        v[u] = __builtin_nontemporal_load(V4 + i);
       }
-      __builtin_nontemporal_store(p[u], P4 + i);
-      __builtin_nontemporal_store(m[u], M4 + i);
-      __builtin_nontemporal_store(v[u], V4 + i);
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = threadIdx.x + 256 * u;
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float mk = m[u][k], vk = v[u][k];
+          p[u][k] = adam_elem(p[u][k], cf * g[u][k], mk, vk, L, lr, wd);
+          m[u][k] = mk; v[u][k] = vk;
+        }
+        __builtin_nontemporal_store(p[u], P4 + i);
+        __builtin_nontemporal_store(m[u], M4 + i);
+        __builtin_nontemporal_store(v[u], V4 + i);
+      }
+    } else {
+      ggu2* M2 = reinterpret_cast<ggu2*>(gmem(static_cast<uint16_t*>(T.m) + c0));
+      ggu2* V2 = reinterpret_cast<ggu2*>(gmem(static_cast<uint16_t*>(T.v) + c0));
+      gu2 mb[2], vb[2];
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        p[u] = __builtin_nontemporal_load(P4 + i);
+        g[u] = __builtin_nontemporal_load(G4 + i);
+        mb[u] = __builtin_nontemporal_load(M2 + i);
+        vb[u] = __builtin_nontemporal_load(V2 + i);
+      }
+#pragma unroll
+      for (int u = 0; u < 2; ++u) {
+        const int i = threadIdx.x + 256 * u;
+        m[u] = widen4(mb[u]);
+        v[u] = widen4(vb[u]);
+#pragma unroll
+        for (int k = 0; k < 4; ++k) {
+          float mk = m[u][k], vk = v[u][k];
+          p[u][k] = adam_elem(p[u][k], cf * g[u][k], mk, vk, L, lr, wd);
+          m[u][k] = mk; v[u][k] = vk;
+        }
+        const int64_t idx = T.index0 + c0 + 4 * static_cast<int64_t>(i);
+        __builtin_nontemporal_store(p[u], P4 + i);
+        __builtin_nontemporal_store(sr_bf16x4(m[u], T.key_m, idx), M2 + i);
+        __builtin_nontemporal_store(sr_bf16x4(v[u], T.key_v, idx), V2 + i);
+      }
     }
-  } else if (vec) {
-    float* P = static_cast<float*>(T.p);
-    const float* G = static_cast<const float*>(T.g);
-    const int64_t nvec_end = c0 + ((c1 - c0) & ~int64_t(3));
-    for (int64_t i = c0 + threadIdx.x * 4; i < nvec_end; i += 256 * 4) {
-      float4 p = *reinterpret_cast<const float4*>(P + i);
-      const float4 g = *reinterpret_cast<const float4*>(G + i);
-      float4 m = *reinterpret_cast<const float4*>(T.m + i);
-      float4 v = *reinterpret_cast<const float4*>(T.v + i);
-      adam_elem(p.x, g.x, m.x, v.x, L, lr, wd);
-      adam_elem(p.y, g.y, m.y, v.y, L, lr, wd);
-      adam_elem(p.z, g.z, m.z, v.z, L, lr, wd);
-      adam_elem(p.w, g.w, m.w, v.w, L, lr, wd);
-      *reinterpret_cast<float4*>(P + i) = p;
-      *reinterpret_cast<float4*>(T.m + i) = m;
-      *reinterpret_cast<float4*>(T.v + i) = v;
-    }
-    for (int64_t i = nvec_end + threadIdx.x; i < c1; i += 256) {
-      float p = P[i], m = T.m[i], v = T.v[i];
-      adam_elem(p, G[i], m, v, L, lr, wd);
-      P[i] = p; T.m[i] = m; T.v[i] = v;
-    }
-  } else {
-    for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
-      float p = load_elem(T.p, i, T.pdt), m = T.m[i], v = T.v[i];
-      adam_elem(p, load_elem(T.g, i, T.gdt), m, v, L, lr, wd);
-      store_elem(T.p, i, T.pdt, p);
-      T.m[i] = m;
-      T.v[i] = v;
+    return;
+  }
+  // Any dtype mix, alignment or chunk length, one element per thread step.
+  for (int64_t i = c0 + threadIdx.x; i < c1; i += 256) {
+    float m = bfm ? bf16_to_f32(gmem(static_cast<const uint16_t*>(T.m))[i]) : gmem(static_cast<const float*>(T.m))[i];
+    float v = bfm ? bf16_to_f32(gmem(static_cast<const uint16_t*>(T.v))[i]) : gmem(static_cast<const float*>(T.v))[i];
+    const float p = adam_elem(load_elem(T.p, i, T.pdt), cf * load_elem(T.g, i, T.gdt), m, v, L, lr, wd);
+    store_elem(T.p, i, T.pdt, p);
+    if (bfm) {
+      gmem(static_cast<uint16_t*>(T.m))[i] = static_cast<uint16_t>(sr_bf16(m, T.key_m, T.index0 + i));
+      gmem(static_cast<uint16_t*>(T.v))[i] = static_cast<uint16_t>(sr_bf16(v, T.key_v, T.index0 + i));
+    } else {
+      gmem(static_cast<float*>(T.m))[i] = m;
+      gmem(static_cast<float*>(T.v))[i] = v;
     }
   }
 }

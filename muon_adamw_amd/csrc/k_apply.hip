@@ -57,6 +57,7 @@ __global__ __launch_bounds__(256) void apply_kernel(const MatDesc* __restrict__ 
   const int blk = blockIdx.x;
   const int e = find_entry(tm, blk);
   const MatDesc& d = mats[tm.perm[e]];
+  if (step_skipped(d.clip)) return;   // the whole block: parameters untouched
   const int t = blk - tm.start[e];
   const int m = d.m, n = d.n;
   const int tiles_n = (n + kEw - 1) / kEw;

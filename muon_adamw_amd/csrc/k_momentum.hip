@@ -48,6 +48,8 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
   const int blk = blockIdx.x;
   const int e = find_entry(tm, blk);
   const MatDesc& d = mats[tm.perm[e]];
+  if (step_skipped(d.clip)) return;   // the whole block: momentum untouched
+  const float cf = clip_factor(d.clip);   // G is read scaled by the global-norm clip
   const int t = blk - tm.start[e];
   const int tiles_c = d.cp / kEw;
   const int i0 = (t / tiles_c) * kEw, j0 = (t % tiles_c) * kEw;   // canonical origin
@@ -69,11 +71,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
       const int64_t idx = (int64_t)(sr0 + tr + 16 * p) * n + sc0 + tc;
       if (d.gdt == DT_BF16) {
         const gu2 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const gu2*>(static_cast<const uint16_t*>(d.grad) + idx)));
-        g[p][0] = __uint_as_float(raw.x << 16); g[p][1] = __uint_as_float(raw.x & 0xffff0000u);
-        g[p][2] = __uint_as_float(raw.y << 16); g[p][3] = __uint_as_float(raw.y & 0xffff0000u);
+        g[p][0] = cf * __uint_as_float(raw.x << 16); g[p][1] = cf * __uint_as_float(raw.x & 0xffff0000u);
+        g[p][2] = cf * __uint_as_float(raw.y << 16); g[p][3] = cf * __uint_as_float(raw.y & 0xffff0000u);
       } else {
         const gf4 raw = __builtin_nontemporal_load(gmem(reinterpret_cast<const gf4*>(static_cast<const float*>(d.grad) + idx)));
-        g[p][0] = raw.x; g[p][1] = raw.y; g[p][2] = raw.z; g[p][3] = raw.w;
+        g[p][0] = cf * raw.x; g[p][1] = cf * raw.y; g[p][2] = cf * raw.z; g[p][3] = cf * raw.w;
       }
       if (d.mom) bm[p] = __builtin_nontemporal_load(gmem(reinterpret_cast<const gf4*>(d.mom + idx)));
     }
@@ -107,7 +109,7 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
           if (sc + u < n) {
-            const float gu = load_elem(d.grad, idx + u, d.gdt);
+            const float gu = cf * load_elem(d.grad, idx + u, d.gdt);
             if (d.mom) {
               float b = gmem(d.mom)[idx + u];
               b = beta * b + omb * gu;
@@ -144,13 +146,13 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
 }
 
 __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ mats, TileMap tm,
-                                                            float eps) {
+                                                            float eps, float scale) {
   __shared__ float red[4];
   const MatDesc& d = mats[tm.perm[blockIdx.x]];
   float s = 0.f;
   for (int i = threadIdx.x; i < d.ntile_ew; i += 256) s += gmem(d.part)[i];
   const float tot = block_sum_256(s, red);
-  if (threadIdx.x == 0) gmem(d.stat)[0] = 1.0f / (sqrtf(tot) + eps);
+  if (threadIdx.x == 0) gmem(d.stat)[0] = 1.0f / (sqrtf(tot) * scale + eps);
 }
 
 }  // namespace
@@ -164,9 +166,9 @@ void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, flo
     hipLaunchKernelGGL(momentum_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
 }
 
-void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, hipStream_t s) {
+void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, float scale, hipStream_t s) {
   if (tm.total == 0) return;
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(tm.grid), dim3(256), 0, s, mats, tm, eps);
+  hipLaunchKernelGGL(norm_finalize_kernel, dim3(tm.grid), dim3(256), 0, s, mats, tm, eps, scale);
 }
 
 }  // namespace ma

@@ -581,10 +581,12 @@ __global__ __launch_bounds__(NTHR, 1) void ns_mfma_kernel(NsArgs args) {
 // nothing is written back. Counters are agent-scope atomics.
 constexpr int kMaxPolls = 1 << 20;
 
-__global__ __launch_bounds__(NTHR, 1) void ns_persistent_kernel(const MatDesc* __restrict__ mats, NsQueue q,
-                                                                float coef_a, float coef_b, float coef_c) {
+__global__ __launch_bounds__(NTHR, 1) void ns_persistent_kernel(const MatDesc* __restrict__ mats, NsQueue q) {
   __shared__ __attribute__((aligned(16))) char smem[SMEM];
   __shared__ int task[4];
+  // a skipped step (global-norm clip state) runs no tile; every block leaves
+  // before touching the queue, so nothing waits on it
+  if (step_skipped(q.clip)) return;
   const int x = __builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20) & 7;   // hwreg(HW_REG_XCC_ID, 0, 4)
   const int4* segs = q.segs + q.seg_off[x];
   const int nseg = q.nseg[x];
@@ -644,6 +646,10 @@ __global__ __launch_bounds__(NTHR, 1) void ns_persistent_kernel(const MatDesc* _
     if (m < 0) break;
     const MatDesc& d = mats[m];
     const int it = itop >> 2, op = itop & 3;
+    // this iteration's (a, b, c)
+    const float coef_a = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(gmem(q.coefs)[3 * it])));
+    const float coef_b = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(gmem(q.coefs)[3 * it + 1])));
+    const float coef_c = __uint_as_float(__builtin_amdgcn_readfirstlane(__float_as_uint(gmem(q.coefs)[3 * it + 2])));
     if (op == OP_GRAM)
       ns_tile_any<OP_GRAM>(d, tile, it & 1, it == 0, coef_a, coef_b, coef_c, smem);
     else if (op == OP_SQUARE)
@@ -662,10 +668,9 @@ __global__ void zero_ints_kernel(int* p, int n) {
 
 }  // namespace
 
-void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, float a, float b, float c,
-                          hipStream_t s) {
+void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, hipStream_t s) {
   hipLaunchKernelGGL(zero_ints_kernel, dim3(16), dim3(256), 0, s, q.qhead, zero_ints);
-  hipLaunchKernelGGL(ns_persistent_kernel, dim3(8 * kPersistBlocksPerXcd), dim3(NTHR), 0, s, mats, q, a, b, c);
+  hipLaunchKernelGGL(ns_persistent_kernel, dim3(8 * kPersistBlocksPerXcd), dim3(NTHR), 0, s, mats, q);
 }
 
 void launch_ns_bf16(int op, const MatDesc* mats, TileMap tm, int src, int first, float a, float b, float c,

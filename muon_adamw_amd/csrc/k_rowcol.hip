@@ -100,6 +100,7 @@ __global__ __launch_bounds__(256) void finalize_normuon_kernel(const MatDesc* __
                                                                float omb2) {
   __shared__ float red[4];
   const MatDesc& d = mats[tm.perm[blockIdx.x]];
+  if (step_skipped(d.clip)) return;   // V untouched
   const float* rs = d.tall ? d.csum_c : d.csum_r;
   const float inv_n = 1.0f / static_cast<float>(d.n);
   float tot = 0.f, toth = 0.f;

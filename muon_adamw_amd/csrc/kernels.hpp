@@ -9,8 +9,8 @@ namespace ma {
 // Frobenius partials (speedtronic "Muon update", first two lines).
 void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, float one_minus_beta,
                      int nesterov, hipStream_t s);
-// sigma = 1 / (sqrt(sum of partials) + eps), one block per matrix, fixed order.
-void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, hipStream_t s);
+// sigma = 1 / (sqrt(sum of partials) * scale + eps), one block per matrix, fixed order.
+void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, float scale, hipStream_t s);
 
 // One product of a Newton-Schulz iteration over every matrix (op 0: Gram
 // A = s2 * X X^T, lower-triangle tiles mirrored; op 1: B = b A + c A A^T, A
@@ -24,8 +24,8 @@ void launch_ns_f32(int op, const MatDesc* mats, TileMap tm, int src, int first, 
 // Every iteration of the bf16 Newton-Schulz chain in one persistent launch
 // (after zeroing the first `zero_ints` ints at q.qhead: the queue heads, the
 // error word and the completion counters).
-void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, float a, float b, float c,
-                          hipStream_t s);
+// The coefficients of iteration it are q.coefs[3 it .. 3 it + 2].
+void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, hipStream_t s);
 
 // Sums of squares of the final Newton-Schulz output along canonical rows
 // (csum_r) or canonical columns (csum_c), optionally weighted by the square
@@ -49,10 +49,13 @@ void launch_apply(const MatDesc* mats, TileMap tm, int ns_dt, int src, int mode,
 struct AdamTensorArg {
   void* p;
   const void* g;
-  float* m;
-  float* v;
+  void* m;            // fp32, or bf16 stored by stochastic rounding
+  void* v;
   int64_t numel;
-  int32_t pdt, gdt;
+  int64_t index0;     // tensor-flat index of element 0 (the rounding counter)
+  uint64_t key_m;     // stochastic-rounding keys of the two moments
+  uint64_t key_v;
+  int32_t pdt, gdt, mdt;
   float lr, wd;
 };
 constexpr int kMaxAdamTensors = 32;
@@ -61,8 +64,39 @@ struct AdamLaunch {
   AdamTensorArg t[kMaxAdamTensors];
   int32_t block_start[kMaxAdamTensors + 1];
   int32_t nt;
+  int32_t cautious;   // keep an entry's update only where update * grad > 0
   float b1, omb1, b2, omb2, eps, inv_bc1, inv_sqrt_bc2;
+  const float* clip;  // global-norm clip state or null
 };
+static_assert(sizeof(AdamLaunch) <= 4000, "kernel argument size");
+// SplitMix64's output function (Steele, Lea and Flood, "Fast splittable
+// pseudorandom number generators", OOPSLA 2014) and its state increment.
+constexpr uint64_t kSplitMixGamma = 0x9E3779B97F4A7C15ull;
+__host__ __device__ inline uint64_t splitmix64_mix(uint64_t z) {
+  z = (z ^ (z >> 30)) * 0xBF58476D1CE4E5B9ull;
+  z = (z ^ (z >> 27)) * 0x94D049BB133111EBull;
+  return z ^ (z >> 31);
+}
 void launch_adamw(const AdamLaunch& L, int nblocks, hipStream_t s);
+
+// Global gradient norm: per-chunk fp32 partial sums of g^2, then one block
+// that adds them in fp64 in a fixed order and writes the clip state.
+struct GradNormArg {
+  const void* g;
+  int64_t numel;
+  int32_t dt;
+  int32_t pad_;
+};
+constexpr int kMaxGradNormTensors = 64;
+constexpr int kGradNormChunk = 8192;   // elements per block
+struct GradNormLaunch {
+  GradNormArg t[kMaxGradNormTensors];
+  int32_t block_start[kMaxGradNormTensors + 1];
+  int32_t nt;
+  float* partial;      // one fp32 per block of all launches
+  int32_t partial_off; // this launch's first partial
+};
+void launch_grad_sumsq(const GradNormLaunch& L, int nblocks, hipStream_t s);
+void launch_grad_norm_finalize(const float* partial, int n, float max_norm, float* state, hipStream_t s);
 
 }  // namespace ma

@@ -18,8 +18,10 @@ Sources, by page title and section:
   is neither moved nor decayed.
 
 Readings where the pages are silent or disagree (each is listed in the design
-notes): normalisation divides by (||X||_F + eps) as on the speedtronic page,
-not by ||g||*1.01; the same (a, b, c) is used in every iteration; "tall" means
+notes): normalisation divides by (||X||_F * s + eps) with s = 1 by default, the
+speedtronic form, and s = 1.01 giving flaxchat's ||g||*1.01 (with its eps); the
+same (a, b, c) is used in every iteration unless a per-iteration table is given
+(flaxchat "Muon Algorithm" step 2 loops over a list of triples); "tall" means
 rows > cols; the shape scale uses the view's own (rows, cols); NorMuon reduces
 over each stored row and rescales to preserve ||U||_F; Muon+ normalises to unit
 L2 norm; the order is NS -> (NorMuon | Muon+) -> scale -> decay/apply.
@@ -45,16 +47,18 @@ def nesterov_lerp(G, B, beta):
 
 
 # -- speedtronic "Newton-Schulz" section ----------------------------------------
-def newton_schulz(M, steps=NS_STEPS, eps=NS_EPS, coeffs=NS_COEFFS):
+def newton_schulz(M, steps=NS_STEPS, eps=NS_EPS, coeffs=NS_COEFFS, table=None, norm_scale=1.0):
     """Quintic Newton-Schulz: transpose a tall matrix, normalise by its Frobenius
-    norm plus eps, iterate A = X X^T; X <- aX + (bA + cA^2)X, transpose back."""
+    norm (times norm_scale) plus eps, iterate A = X X^T; X <- aX + (bA + cA^2)X,
+    transpose back. ``table``: one (a, b, c) per iteration, else ``coeffs`` for
+    every iteration."""
     X = np.array(M, dtype=np.float64, copy=True)
     tall = X.shape[0] > X.shape[1]
     if tall:
         X = X.T
-    X = X / (np.linalg.norm(X) + eps)
-    a, b, c = coeffs
-    for _ in range(steps):
+    X = X / (np.linalg.norm(X) * norm_scale + eps)
+    for i in range(steps):
+        a, b, c = coeffs if table is None else table[i]
         A = X @ X.T
         B = b * A + c * (A @ A)
         X = a * X + B @ X
@@ -114,7 +118,7 @@ def matrix_update(Q, W, G, V, hp, lr, wd):
     """
     m, n = Q.shape
     U = newton_schulz(Q, hp.get("ns_steps", NS_STEPS), hp.get("ns_eps", NS_EPS),
-                      hp.get("ns_coeffs", NS_COEFFS))
+                      hp.get("ns_coeffs", NS_COEFFS), hp.get("ns_table"), hp.get("ns_norm_scale", 1.0))
     U_dir = U
     V_new = V
     if hp.get("normuon", False):
@@ -167,8 +171,13 @@ def muon_tensor_step(W, G, B, V, views, hp, lr, wd):
     return W_new, B_new, V_new, U_all
 
 
-def muon_step(tensors, hp):
+def muon_step(tensors, hp, clip=None):
     """Whole Muon half of the hybrid step.
+
+    ``clip``: (factor, skip) from the global-norm clip (oracle.gradnorm), or
+    None. The gradient enters scaled by the factor; a skipped step returns
+    every stored input unchanged (kimi-k3 "Optimization": an overflow skips the
+    whole hybrid update).
 
     ``tensors``: list of dicts with stored inputs
       param (array, float32 or bf16 bits), param_dtype, grad (or None),
@@ -182,6 +191,13 @@ def muon_step(tensors, hp):
         shape = t["shape"]
         W = storage.decode(t["param"], t["param_dtype"]).reshape(shape)
         G = None if t["grad"] is None else storage.decode(t["grad"], t["grad_dtype"]).reshape(shape)
+        if clip is not None and clip[1]:
+            out.append({"param": np.array(t["param"], copy=True), "momentum": np.array(t["momentum"], copy=True),
+                        "row_v": None if t.get("row_v") is None else np.array(t["row_v"], copy=True),
+                        "W64": None, "B64": None, "V64": None, "U64": None})
+            continue
+        if clip is not None and G is not None:
+            G = clip[0] * G
         B = storage.decode(t["momentum"], "f32").reshape(shape)
         V = None if t.get("row_v") is None else storage.decode(t["row_v"], "f32").reshape(shape[0], shape[1])
         W_new, B_new, V_new, U = muon_tensor_step(W, G, B, V, t.get("views", 1), hp, t["lr"], t["wd"])

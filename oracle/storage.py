@@ -57,3 +57,46 @@ def round_to(x, dtype: str) -> np.ndarray:
     if dtype == "bf16":
         return round_bf16_bits(x)
     raise ValueError(f"unknown dtype {dtype!r}")
+
+
+# -- dew.training.optim "stochastic_round_bf16" -------------------------------
+# The pages name no hash ("a counter-based hash" of the seed and each element's
+# flat index). The one used is SplitMix64 (Steele, Lea and Flood, "Fast
+# splittable pseudorandom number generators", OOPSLA 2014): state advanced by
+# the golden-ratio increment, output function mix64 below.
+SPLITMIX_GAMMA = 0x9E3779B97F4A7C15
+_M64 = (1 << 64) - 1
+
+
+def splitmix64_mix(z):
+    """SplitMix64's output function on uint64 values (array or int)."""
+    z = np.asarray(z, dtype=np.uint64)
+    with np.errstate(over="ignore"):   # arithmetic modulo 2^64 is the definition
+        z = (z ^ (z >> np.uint64(30))) * np.uint64(0xBF58476D1CE4E5B9)
+        z = (z ^ (z >> np.uint64(27))) * np.uint64(0x94D049BB133111EB)
+    return z ^ (z >> np.uint64(31))
+
+
+def sr_key(seed, step, leaf, moment):
+    """Key of one (step, tensor, moment) stream: mix(seed ^ mix((step << 32) +
+    (leaf << 1) + moment)), all modulo 2^64."""
+    c = ((int(step) << 32) + (int(leaf) << 1) + int(moment)) & _M64
+    return int(splitmix64_mix(np.uint64(int(seed) & _M64) ^ splitmix64_mix(np.uint64(c))))
+
+
+def stochastic_round_bf16_bits(x32, key, index0=0):
+    """binary32 values -> bf16 bit patterns: add 16 uniform bits below the kept
+    mantissa and truncate, so a value rounds up with the probability of its
+    distance from the lower neighbour; NaN stays NaN (a quiet NaN). The bits
+    of element i (flat index index0 + i) are the top 16 of SplitMix64's output
+    at state key + (index0 + i + 1) * gamma."""
+    x32 = np.ascontiguousarray(np.asarray(x32, dtype=np.float32))
+    u = x32.reshape(-1).view(np.uint32).astype(np.uint64)
+    idx = np.arange(u.size, dtype=np.uint64) + np.uint64(int(index0) + 1)
+    with np.errstate(over="ignore"):
+        state = np.uint64(int(key) & _M64) + idx * np.uint64(SPLITMIX_GAMMA)
+    r = splitmix64_mix(state) >> np.uint64(48)
+    out = ((u + r) >> np.uint64(16)).astype(np.uint16)
+    nan = (u & np.uint64(0x7FFFFFFF)) > np.uint64(0x7F800000)
+    out[nan] = ((u[nan] >> np.uint64(16)) | np.uint64(0x40)).astype(np.uint16)
+    return out.reshape(x32.shape)

@@ -276,8 +276,8 @@ def test_config2_adamw():
 
 
 def test_adamw_two_steps_bf16_params_and_tail():
-    """bf16 params/grads, a ragged length, two steps; step 2 is checked against
-    the oracle fed the GPU's stored state after step 1."""
+    """bf16 params/grads, a ragged length, two steps; each side continues from
+    its own stored state after step 1."""
     n = 100003
     p = randn((n,), 1, 0.02).to(torch.bfloat16)
     g1 = randn((n,), 2, 1e-3).to(torch.bfloat16)
@@ -291,11 +291,12 @@ def test_adamw_two_steps_bf16_params_and_tail():
     assert rel(host(P.m), m1) < 1e-6 and rel(host(P.v), v1) < 1e-6
     bits = workloads.to_numpy(P.param).astype(np.int32)
     assert np.abs(bits - storage.round_bf16_bits(p1).astype(np.int32)).max() <= 1
-    p1g, m1g, v1g = host(P.param), host(P.m), host(P.v)
+    p1o = storage.decode(storage.round_bf16_bits(p1), "bf16")
+    m1o, v1o = storage.round_f32(m1).astype(np.float64), storage.round_f32(v1).astype(np.float64)
     P.grad = g2.to(DEV)
     ma.adamw_step([P], 0.9, 0.999, 1e-8, 2)
     torch.cuda.synchronize()
-    p2, m2, v2 = oadamw.adamw_update(p1g, host(g2), m1g, v1g, 1e-3, 0.05, 0.9, 0.999, 1e-8, 2)
+    p2, m2, v2 = oadamw.adamw_update(p1o, host(g2), m1o, v1o, 1e-3, 0.05, 0.9, 0.999, 1e-8, 2)
     assert rel(host(P.m), m2) < 1e-6 and rel(host(P.v), v2) < 1e-6
     bits = workloads.to_numpy(P.param).astype(np.int32)
     assert np.abs(bits - storage.round_bf16_bits(p2).astype(np.int32)).max() <= 1
@@ -412,26 +413,29 @@ def test_views_match_separate_tensors_bitwise():
 
 
 def test_two_steps_continue_from_state():
-    """Step, then step again: equals the oracle's second step fed the GPU's
-    state after the first; and saving/restoring the state in between changes
-    nothing (bitwise)."""
+    """Step, then step again: the GPU's second step equals the oracle's second
+    step, each side continuing from its own stored state; and saving/restoring
+    the GPU state in between changes nothing (bitwise)."""
     wl = small_workload(ns_dtype="f32")
     h = hp_dict(wl.muon_hp)
     data = to_gpu(workloads.generate(wl, device="cpu"))
+    inp1 = oracle_inputs(data)
     hp = hp_c(wl.muon_hp)
     ma.muon_step(muon_params(data), hp)
     torch.cuda.synchronize()
+    want1 = omuon.muon_step(inp1, h)
     saved = [(t.param.cpu().clone(), t.momentum.cpu().clone()) for t in data.muon]
     for t in data.muon:
         t.grad = torch.randn(t.grad.shape, generator=torch.Generator().manual_seed(99)).to(DEV)
-    inp = oracle_inputs(data)
+    inp2 = [dict(i, param=w["param"], momentum=w["momentum"], grad=workloads.to_numpy(t.grad.cpu()))
+            for i, w, t in zip(inp1, want1, data.muon)]
     # a copy restored from host state
     clone = [ma.MuonParam(p.to(DEV), t.grad, m.to(DEV), None, t.spec.views, t.spec.lr, t.spec.wd)
              for (p, m), t in zip(saved, data.muon)]
     ma.muon_step(muon_params(data), hp)
     ma.muon_step(clone, hp)
     torch.cuda.synchronize()
-    want = omuon.muon_step(inp, h)
+    want = omuon.muon_step(inp2, h)
     for t, c, w in zip(data.muon, clone, want):
         assert torch.equal(t.param, c.param) and torch.equal(t.momentum, c.momentum)
         check_momentum(t.momentum, w["momentum"])

@@ -32,27 +32,27 @@ def _ns_template(M, steps=5, eps=1e-7, coeffs=(A, B, C), *, wrong_side=False,
     return X.T if tall else X
 
 
-def ns_flip_b(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+def ns_flip_b(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     return _ns_template(M, steps, eps, (A, -B, C))
 
 
-def ns_drop_c(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+def ns_drop_c(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     return _ns_template(M, steps, eps, (A, B, 0.0))
 
 
-def ns_spectral(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+def ns_spectral(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     return _ns_template(M, steps, eps, coeffs, spectral=True)
 
 
-def ns_no_eps(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+def ns_no_eps(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     return _ns_template(M, steps, eps, coeffs, drop_eps=True)
 
 
-def ns_four_steps(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+def ns_four_steps(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     return _ns_template(M, steps, eps, coeffs, steps_delta=-1)
 
 
-def ns_xa_order(M, steps=5, eps=1e-7, coeffs=(A, B, C)):
+def ns_xa_order(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     """X (bA + cA^2) instead of (bA + cA^2) X: the operands swap places, which
     only type-checks (and only differs) for a square matrix."""
     X = np.array(M, dtype=np.float64)
@@ -292,3 +292,82 @@ def bf16_via_f32(x):
 def test_bf16_rounding_mutants_caught(mutant):
     with pytest.raises(AssertionError):
         pins.check_bf16_rounding(mutant)
+
+
+
+# -- next rows: stochastic rounding, cautious AdamW, global norm, NS table ---
+from oracle import adamw as oadamw  # noqa: E402
+from oracle import gradnorm as ognorm  # noqa: E402
+from oracle import storage as ostorage  # noqa: E402
+
+
+def _sr_wide_noise(x32, key, index0=0):
+    """17 noise bits instead of 16: rounds up too often."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    u = x32.reshape(-1).view(np.uint32).astype(np.uint64)
+    idx = np.arange(u.size, dtype=np.uint64) + np.uint64(index0 + 1)
+    with np.errstate(over="ignore"):
+        r = ostorage.splitmix64_mix(np.uint64(key) + idx * np.uint64(ostorage.SPLITMIX_GAMMA)) >> np.uint64(47)
+    return ((u + r) >> np.uint64(16)).astype(np.uint16).reshape(x32.shape)
+
+
+def _sr_no_nan_rule(x32, key, index0=0):
+    """Plain add-and-truncate, NaN not special-cased."""
+    x32 = np.asarray(x32, dtype=np.float32)
+    u = x32.reshape(-1).view(np.uint32).astype(np.uint64)
+    idx = np.arange(u.size, dtype=np.uint64) + np.uint64(index0 + 1)
+    with np.errstate(over="ignore"):
+        r = ostorage.splitmix64_mix(np.uint64(key) + idx * np.uint64(ostorage.SPLITMIX_GAMMA)) >> np.uint64(48)
+    return ((u + r) >> np.uint64(16)).astype(np.uint16).reshape(x32.shape)
+
+
+@pytest.mark.parametrize("mutant", [_sr_wide_noise, _sr_no_nan_rule], ids=lambda f: f.__name__)
+def test_stochastic_rounding_mutants_caught(mutant, monkeypatch):
+    monkeypatch.setattr(ostorage, "stochastic_round_bf16_bits", mutant)
+    with pytest.raises(AssertionError):
+        pins.test_stochastic_rounding_keeps_exact_values_and_specials()
+        for f in (0.1, 0.25, 0.5, 0.9):
+            pins.test_stochastic_rounding_probability_is_distance(f)
+
+
+def _adamw_cautious_ge(p, g, m, v, lr, wd, beta1, beta2, eps, step, cautious=False):
+    p2, m2, v2 = oadamw_orig(p, g, m, v, lr, wd, beta1, beta2, eps, step)
+    if cautious:
+        p2 = np.where((p - p2) * g >= 0.0, p2, p)
+    return p2, m2, v2
+
+
+def _adamw_cautious_after_update(p, g, m, v, lr, wd, beta1, beta2, eps, step, cautious=False):
+    """Mask from the new parameter instead of the observed update."""
+    p2, m2, v2 = oadamw_orig(p, g, m, v, lr, wd, beta1, beta2, eps, step)
+    if cautious:
+        p2 = np.where(p2 * g > 0.0, p2, p)
+    return p2, m2, v2
+
+
+oadamw_orig = oadamw.adamw_update
+
+
+@pytest.mark.parametrize("mutant", [_adamw_cautious_ge, _adamw_cautious_after_update], ids=lambda f: f.__name__)
+def test_cautious_adamw_mutants_caught(mutant, monkeypatch):
+    monkeypatch.setattr(oadamw, "adamw_update", mutant)
+    with pytest.raises(AssertionError):
+        pins.test_cautious_adamw_masks_against_the_gradient()
+
+
+def test_grad_norm_without_sqrt_caught(monkeypatch):
+    orig = ognorm.global_norm
+    monkeypatch.setattr(ognorm, "global_norm", lambda grads: orig(grads) ** 2)
+    with pytest.raises(AssertionError):
+        pins.test_global_norm_and_clip_closed_forms()
+
+
+def test_ns_table_reversed_caught(monkeypatch):
+    orig = omuon.newton_schulz
+
+    def reversed_table(M, steps=5, eps=1e-7, coeffs=omuon.NS_COEFFS, table=None, norm_scale=1.0):
+        return orig(M, steps, eps, coeffs, None if table is None else list(table)[::-1], norm_scale)
+
+    monkeypatch.setattr(omuon, "newton_schulz", reversed_table)
+    with pytest.raises(AssertionError):
+        pins.test_ns_table_closed_forms_and_order()

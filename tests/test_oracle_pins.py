@@ -431,3 +431,185 @@ def test_muon_step_dict_api_bf16():
     assert np.abs(out["W64"][0] - want).max() < 1e-14
     assert np.array_equal(out["param"], storage.round_bf16_bits(out["W64"]))
     assert np.array_equal(out["momentum"], (0.05 * G64).astype(np.float32))
+
+
+# ---------------------------------------------------------------------------
+# Next rows: stochastic rounding, bf16 moments, global-norm clip, cautious
+# AdamW, per-iteration coefficients
+# ---------------------------------------------------------------------------
+from oracle import gradnorm as ognorm  # noqa: E402
+
+
+def test_splitmix64_reference_outputs():
+    """SplitMix64 (Steele, Lea and Flood 2014) seeded with 0 yields
+    0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F: the published
+    generator's first outputs, state advanced by the golden-ratio gamma."""
+    g = storage.SPLITMIX_GAMMA
+    got = [int(storage.splitmix64_mix(np.uint64((k * g) % 2**64))) for k in (1, 2, 3)]
+    assert got == [0xE220A8397B1DCDAF, 0x6E789E6AA1B965F4, 0x06C45D188009454F]
+
+
+def test_stochastic_rounding_keeps_exact_values_and_specials():
+    """A value already in bf16 has zero discarded bits: no noise can carry, so
+    it is kept for every key; infinities stay infinite; NaN stays NaN
+    (dew.training.optim "stochastic_round_bf16")."""
+    rng = np.random.default_rng(3)
+    bits = rng.integers(0, 0x7F7F, size=5000).astype(np.uint16)
+    bits[::2] |= 0x8000
+    x = storage.decode(bits, "bf16").astype(np.float32)
+    for key in (0, 1, 0xDEADBEEFCAFEF00D):
+        assert np.array_equal(storage.stochastic_round_bf16_bits(x, key), bits)
+    sp = np.array([np.inf, -np.inf, np.nan, -np.nan], dtype=np.float32)
+    # NaNs whose payload sits only in the discarded low bits must not truncate to inf
+    sp = np.concatenate([sp, np.array([0x7F800001, 0xFF80FFFF], dtype=np.uint32).view(np.float32)])
+    out = storage.stochastic_round_bf16_bits(sp, 7)
+    assert out[0] == 0x7F80 and out[1] == 0xFF80
+    back = storage.decode(out, "bf16")
+    assert np.isnan(back[2:]).all()
+
+
+@pytest.mark.parametrize("frac", [0.1, 0.25, 0.5, 0.9])
+def test_stochastic_rounding_probability_is_distance(frac):
+    """x between two bf16 neighbours rounds up with probability equal to its
+    fractional distance from the lower one (the page: "rounded ... up or down
+    with the probability of its distance to each"), over 40000 flat indices."""
+    lo = np.float32(1.5)
+    ulp = np.float32(2.0 ** -7)          # bf16 spacing in [1, 2)
+    x = np.full(40000, lo + np.float32(frac) * ulp, dtype=np.float32)
+    out = storage.decode(storage.stochastic_round_bf16_bits(x, 12345), "bf16")
+    assert set(np.unique(out)) <= {float(lo), float(lo + ulp)}
+    p_up = np.mean(out > lo)
+    sigma = math.sqrt(frac * (1 - frac) / x.size)
+    assert abs(p_up - frac) < 5 * sigma + 1e-4, (p_up, frac)
+
+
+def test_bf16_second_moment_increments_kept_in_expectation():
+    """The page's reason for stochastic rounding: with beta2 = 0.999 most
+    increments of the second moment are below half its bf16 spacing, so
+    round-to-nearest loses them all, while the stochastic rounding keeps each
+    one in expectation. v = 1 (exact in bf16), g^2 = 1.5: the increment is
+    0.0005, about a sixteenth of the spacing 2^-7."""
+    v0, g2, b2 = 1.0, 1.5, 0.999
+    v1 = b2 * v0 + (1 - b2) * g2
+    rne = storage.decode(storage.round_bf16_bits(np.array([v1])), "bf16")[0]
+    assert rne == v0                                  # nearest rounding loses it
+    x = np.full(200000, np.float32(v1), dtype=np.float32)
+    sr = storage.decode(storage.stochastic_round_bf16_bits(x, 99), "bf16")
+    mean_inc = float(np.mean(sr) - v0)
+    assert abs(mean_inc - (v1 - v0)) < 5 * math.sqrt((v1 - v0) * 2 ** -7 / x.size) + 1e-7
+
+
+def test_adamw_bf16_moments_use_the_step_tensor_and_moment_keys():
+    """bf16 moments: the update runs on the widened moments; each new moment is
+    the fp32 value stochastically rounded with the key of (seed, step, tensor,
+    moment); different tensors, moments or steps draw different bits."""
+    rng = np.random.default_rng(8)
+    n = 5000
+    t = lambda: {"param": rng.normal(0, 0.02, n).astype(np.float32), "param_dtype": "f32",
+                 "grad": rng.normal(0, 1e-3, n).astype(np.float32), "grad_dtype": "f32",
+                 "m": storage.round_bf16_bits(rng.normal(0, 1e-4, n)),
+                 "v": storage.round_bf16_bits(rng.uniform(1e-8, 1e-6, n)), "moment_dtype": "bf16",
+                 "lr": 1e-3, "wd": 0.1}
+    ts = [t(), t()]
+    hp = {"beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "step": 3, "seed": 42}
+    out = oadamw.adamw_step(ts, hp)
+    for k, (ti, o) in enumerate(zip(ts, out)):
+        p64, m64, v64 = oadamw.adamw_update(storage.decode(ti["param"], "f32"), storage.decode(ti["grad"], "f32"),
+                                            storage.decode(ti["m"], "bf16"), storage.decode(ti["v"], "bf16"),
+                                            1e-3, 0.1, 0.9, 0.999, 1e-8, 3)
+        assert np.array_equal(o["param"], storage.round_f32(p64))
+        # each stored moment is one of the two bf16 neighbours of its fp32 value
+        for nm, x64 in (("m", m64), ("v", v64)):
+            x32 = storage.round_f32(x64).astype(np.float64)
+            got = storage.decode(o[nm], "bf16")
+            lo = storage.decode((np.asarray(storage.round_f32(x64)).view(np.uint32) >> 16).astype(np.uint16), "bf16")
+            assert np.all((got == lo) | (np.abs(got) > np.abs(lo))) and np.all(np.abs(got - x32) <= np.abs(x32) * 2 ** -7)
+    assert not np.array_equal(out[0]["m"], oadamw.adamw_step([ts[0]], dict(hp, step=4))[0]["m"])
+
+
+def test_global_norm_and_clip_closed_forms():
+    """||g|| over every element of every gradient; the clip factor is
+    max_norm/||g|| above max_norm, 1 below it or with max_norm <= 0 (clipping
+    off, the norm still observed); a norm that is not finite skips the step."""
+    a = np.ones(300, dtype=np.float32)
+    b = storage.round_bf16_bits(np.full((10, 10), 2.0))
+    nrm = ognorm.global_norm([(a, "f32"), None, (b, "bf16")])
+    assert nrm == math.sqrt(300 + 400)
+    assert ognorm.clip_state(nrm, 10.0) == (10.0 / math.sqrt(700), False)
+    assert ognorm.clip_state(nrm, 100.0) == (1.0, False)
+    assert ognorm.clip_state(nrm, 0.0) == (1.0, False)
+    big = np.array([1e30, 1e30], dtype=np.float32)
+    assert ognorm.clip_state(ognorm.global_norm([(big, "f32")]), 1.0)[1] is False   # finite in fp64
+    inf = np.array([np.inf], dtype=np.float32)
+    nan = np.array([np.nan], dtype=np.float32)
+    assert ognorm.clip_state(ognorm.global_norm([(inf, "f32")]), 1.0)[1] is True
+    assert ognorm.clip_state(ognorm.global_norm([(nan, "f32")]), 0.0)[1] is True
+
+
+def test_clip_skip_leaves_every_buffer_and_scales_the_gradient():
+    """A skipped step returns every stored input unchanged (both halves); a
+    clip factor enters as a scaled gradient: from zero momentum the new
+    momentum is (1 - beta) * factor * G."""
+    rng = np.random.default_rng(5)
+    W = rng.normal(0, 0.02, (1, 40, 60)).astype(np.float32)
+    G = rng.normal(0, 1e-3, (1, 40, 60)).astype(np.float32)
+    t = {"param": W, "param_dtype": "f32", "grad": G, "grad_dtype": "f32",
+         "momentum": np.zeros_like(W), "row_v": None, "views": 1, "lr": 0.02, "wd": 0.1, "shape": (1, 40, 60)}
+    out = omuon.muon_step([t], {"ns_steps": 5}, clip=(0.25, True))[0]
+    assert np.array_equal(out["param"], W) and np.array_equal(out["momentum"], t["momentum"])
+    out = omuon.muon_step([t], {"ns_steps": 5, "beta": 0.95}, clip=(0.25, False))[0]
+    assert np.allclose(out["B64"], 0.05 * 0.25 * G.astype(np.float64), rtol=1e-14, atol=0)
+    a = {"param": W.ravel(), "param_dtype": "f32", "grad": G.ravel(), "grad_dtype": "f32",
+         "m": np.zeros(W.size, np.float32), "v": np.zeros(W.size, np.float32), "lr": 1e-3, "wd": 0.1}
+    o = oadamw.adamw_step([a], {"beta1": 0.9, "beta2": 0.95, "eps": 1e-8, "step": 1}, clip=(1.0, True))[0]
+    assert np.array_equal(o["param"], a["param"]) and np.array_equal(o["m"], a["m"])
+
+
+def test_cautious_adamw_masks_against_the_gradient():
+    """speedtronic "Cautious updates" over AdamW. At step 1 with zero state,
+    m_hat = g and v_hat = g^2, so the update is lr (g/(|g|+eps) + wd p): with
+    wd = 0 it always points along g (nothing masked); with a large decay on a
+    parameter of opposite sign to g it points against g, and that parameter
+    is left bit for bit; the moments are updated everywhere."""
+    g = np.array([1e-3, -2e-3, 1e-3, -1e-3, 0.0])
+    p = np.array([0.5, 0.5, -100.0, 100.0, 0.5])
+    z = np.zeros(5)
+    p0, m0, v0 = oadamw.adamw_update(p, g, z, z, 1e-2, 0.0, 0.9, 0.999, 1e-8, 1)
+    p1, m1, v1 = oadamw.adamw_update(p, g, z, z, 1e-2, 0.0, 0.9, 0.999, 1e-8, 1, cautious=True)
+    assert np.array_equal(p0, p1)
+    # a zero gradient: the update is pure decay, not > 0 against g = 0: kept as is
+    pz, _, _ = oadamw.adamw_update(p, g, z, z, 1e-2, 0.1, 0.9, 0.999, 1e-8, 1, cautious=True)
+    assert pz[4] == p[4]
+    p2, m2, v2 = oadamw.adamw_update(p, g, z, z, 1e-2, 0.1, 0.9, 0.999, 1e-8, 1, cautious=True)
+    # entries 2, 3: 1 + 0.1 * p has the opposite sign of g -> masked
+    assert p2[2] == p[2] and p2[3] == p[3]
+    assert p2[0] < p[0] and p2[1] < p[1] + 1.0
+    assert np.array_equal(m2, m0) and np.array_equal(v2, v0)
+
+
+def test_ns_table_closed_forms_and_order():
+    """Per-iteration coefficients, against the SVD X0 = U S V^T of the
+    normalised input: a row (s, 0, 0) scales X by s; (0, 1, 0) maps S to S^3;
+    (0, 0, 1) maps S to S^5. So [(2,0,0), (0,1,0), (0,0,1)] gives
+    U (2S)^15 V^T... i.e. singular values (8 S^3)^5, and the reversed table
+    gives 2 S^15: each row is used at its own iteration."""
+    rng = np.random.default_rng(11)
+    M = rng.normal(size=(20, 30))
+    X0 = M / np.linalg.norm(M)
+    U, S, Vt = np.linalg.svd(X0, full_matrices=False)
+    fwd = omuon.newton_schulz(M, steps=3, eps=0.0, table=[(2, 0, 0), (0, 1, 0), (0, 0, 1)])
+    rev = omuon.newton_schulz(M, steps=3, eps=0.0, table=[(0, 0, 1), (0, 1, 0), (2, 0, 0)])
+    assert np.allclose(fwd, (U * (8 * S ** 3) ** 5) @ Vt, rtol=1e-10, atol=1e-300)
+    assert np.allclose(rev, (U * (2 * S ** 15)) @ Vt, rtol=1e-10, atol=1e-300)
+    # a constant table is the plain iteration
+    plain = omuon.newton_schulz(M)
+    assert np.array_equal(omuon.newton_schulz(M, table=[omuon.NS_COEFFS] * 5), plain)
+
+
+def test_ns_norm_scale_is_flaxchat_safety_factor():
+    """flaxchat "Muon Algorithm" step 2 starts from g / (||g|| * 1.01): with one
+    identity iteration (1, 0, 0) the output is exactly that, plus eps."""
+    rng = np.random.default_rng(12)
+    M = rng.normal(size=(16, 24))
+    out = omuon.newton_schulz(M, steps=1, eps=1e-7, table=[(1, 0, 0)], norm_scale=1.01)
+    assert np.allclose(out, M / (np.linalg.norm(M) * 1.01 + 1e-7), rtol=1e-14, atol=0)
