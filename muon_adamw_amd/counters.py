@@ -33,6 +33,7 @@ _NAMES = [
     (r"apply_kernel", "apply_update"), (r"adamw_kernel", "adamw"),
     (r"canon_rowsum_kernel", "rowsum"), (r"canon_colsum_kernel", "colsum"),
     (r"finalize_normuon_kernel", "finalize_normuon"), (r"finalize_muon_plus_kernel", "finalize_muon_plus"),
+    (r"grad_sumsq_kernel", "grad_sumsq"), (r"grad_norm_finalize_kernel", "grad_norm_finalize"),
 ]
 
 

@@ -57,6 +57,9 @@ int main(void) {{
   S(ma_muon_hparams); O(ma_muon_hparams, normuon_beta2); O(ma_muon_hparams, ns_dtype); O(ma_muon_hparams, cautious);
   S(ma_adamw_tensor); O(ma_adamw_tensor, numel); O(ma_adamw_tensor, weight_decay);
   S(ma_adamw_hparams); O(ma_adamw_hparams, step);
+  O(ma_muon_hparams, ns_table); O(ma_muon_hparams, clip); O(ma_muon_hparams, ns_norm_scale);
+  O(ma_adamw_tensor, moment_dtype); O(ma_adamw_hparams, cautious); O(ma_adamw_hparams, seed);
+  O(ma_adamw_hparams, clip); S(ma_grad_ref); O(ma_grad_ref, dtype);
   S(ma_matrix_info); O(ma_matrix_info, scale); O(ma_matrix_info, u_offset);
   O(ma_matrix_info, a_offset); O(ma_matrix_info, b_offset);
   return 0;
@@ -80,6 +83,15 @@ int main(void) {{
         "ma_adamw_tensor.weight_decay": ma.AdamWTensorC.weight_decay.offset,
         "ma_adamw_hparams": ctypes.sizeof(ma.AdamWHParamsC),
         "ma_adamw_hparams.step": ma.AdamWHParamsC.step.offset,
+        "ma_muon_hparams.ns_table": ma.MuonHParamsC.ns_table.offset,
+        "ma_muon_hparams.clip": ma.MuonHParamsC.clip.offset,
+        "ma_muon_hparams.ns_norm_scale": ma.MuonHParamsC.ns_norm_scale.offset,
+        "ma_adamw_tensor.moment_dtype": ma.AdamWTensorC.moment_dtype.offset,
+        "ma_adamw_hparams.cautious": ma.AdamWHParamsC.cautious.offset,
+        "ma_adamw_hparams.seed": ma.AdamWHParamsC.seed.offset,
+        "ma_adamw_hparams.clip": ma.AdamWHParamsC.clip.offset,
+        "ma_grad_ref": ctypes.sizeof(ma.GradRefC),
+        "ma_grad_ref.dtype": ma.GradRefC.dtype.offset,
         "ma_matrix_info": ctypes.sizeof(ma.MatrixInfoC),
         "ma_matrix_info.scale": ma.MatrixInfoC.scale.offset,
         "ma_matrix_info.u_offset": ma.MatrixInfoC.u_offset.offset,
@@ -260,6 +272,51 @@ def test_adamw_validation(lib):
     t[0].grad = None
     t[1].grad = None
     assert lib.adamw_step(t, 2, ctypes.byref(good), None) == 0   # nothing to do
+
+
+def test_next_row_validation(lib):
+    """The clip state, the coefficient table, bf16 moments and cautious AdamW
+    are validated before anything is enqueued (no GPU is touched here)."""
+    wl = workloads.workload(2)
+    n = len(wl.muon)
+    # a table entry that is not finite; a negative norm scale; a misaligned clip state
+    assert step(lib, fake_descs(wl), n, ma.muon_hparams(ns_table=[(1.0, 2.0, float("nan"))] + [(1, 0, 0)] * 4)) == 1
+    assert b"ns_table" in lib.ma_last_error()
+    assert step(lib, fake_descs(wl), n, ma.muon_hparams(ns_norm_scale=-1.0)) == 1
+    assert step(lib, fake_descs(wl), n, ma.muon_hparams(clip=BASE + 4)) == 1
+    t = (ma.AdamWTensorC * 1)()
+    t[0].param, t[0].grad, t[0].m, t[0].v = BASE, BASE + (1 << 34), BASE + (2 << 34), BASE + (3 << 34)
+    t[0].numel, t[0].lr, t[0].weight_decay = 1000, 3e-4, 0.1
+    hp = ma.AdamWHParamsC(0.9, 0.95, 1e-8, 1)
+    hp.cautious = 1                                   # Muon's weight-decay mask
+    assert lib.adamw_step(t, 1, ctypes.byref(hp), None) == 5
+    hp.cautious = 3
+    assert lib.adamw_step(t, 1, ctypes.byref(hp), None) == 1
+    hp.cautious = 0
+    hp.clip = BASE + 8
+    assert lib.adamw_step(t, 1, ctypes.byref(hp), None) == 1
+    hp.clip = None
+    t[0].moment_dtype = 7
+    assert lib.adamw_step(t, 1, ctypes.byref(hp), None) == 2
+    t[0].moment_dtype = ma.MA_BF16
+    t[0].m = BASE + (2 << 34) + 1                     # bf16 moments need 2-byte alignment
+    assert lib.adamw_step(t, 1, ctypes.byref(hp), None) == 1
+    # bf16 moments occupy 2 bytes per element: ranges 2000 bytes apart do not overlap
+    t[0].m, t[0].v = BASE + (2 << 34), BASE + (2 << 34) + 2000
+    t[0].grad = None
+    assert lib.adamw_step(t, 1, ctypes.byref(hp), None) == 0
+    # global norm: workspace size, alignment, state alignment, dtype
+    g = (ma.GradRefC * 3)()
+    for i in range(3):
+        g[i].grad, g[i].numel, g[i].dtype = BASE + i * (1 << 30), 10000 + i, ma.MA_F32
+    need = lib.ma_grad_norm_workspace_bytes(g, 3)
+    assert need >= 3 * 2 * 4 and need % 256 == 0
+    assert lib.ma_global_grad_norm(g, 3, 1.0, BASE + 8, BASE, need, None) == 1
+    assert lib.ma_global_grad_norm(g, 3, 1.0, BASE, BASE, need - 256 if need > 256 else 0, None) == 4
+    assert lib.ma_global_grad_norm(g, 3, 1.0, BASE, BASE + 16, need, None) == 4
+    assert lib.ma_global_grad_norm(g, 3, float("inf"), BASE, BASE, need, None) == 1
+    g[1].dtype = 5
+    assert lib.ma_global_grad_norm(g, 3, 1.0, BASE, BASE, need, None) == 2
 
 
 def test_newton_schulz_workspace_query(lib):
