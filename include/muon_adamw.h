@@ -151,7 +151,9 @@ typedef struct {
 
 /* Device bytes of workspace muon_step needs for this tensor list (host call,
  * no GPU work). Returns 0 and sets ma_last_error() if the arguments are
- * invalid. */
+ * invalid. Also returns 0, with ma_last_error() untouched, when no tensor has a
+ * gradient: muon_step then has nothing to do and needs no workspace (NULL is
+ * accepted). */
 size_t ma_muon_workspace_bytes(const ma_muon_tensor* tensors, int32_t n,
                                const ma_muon_hparams* hp);
 

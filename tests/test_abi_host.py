@@ -248,6 +248,8 @@ def test_absent_gradients_make_an_empty_step(lib):
     hp = hp_of(wl)
     assert counts(lib, arr, len(wl.muon), hp)[1] == 0
     assert lib.ma_muon_workspace_bytes(arr, len(wl.muon), ctypes.byref(hp)) == 0
+    # nothing to do: no workspace needed, nothing enqueued, status OK
+    assert step(lib, arr, len(wl.muon), hp) == 0
     assert step(lib, arr, len(wl.muon), hp) == 0     # nothing to do, no GPU call
 
 
