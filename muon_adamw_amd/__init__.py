@@ -151,6 +151,24 @@ def _check_dense(t: torch.Tensor, what: str):
         raise ValueError(f"{what}: tensor must be contiguous")
 
 
+def _check_device(t: torch.Tensor, device, what: str):
+    """Every pointer of a call must be memory of the one GPU the kernels run
+    on: a host or other-device tensor would be dereferenced by the GPU."""
+    if t.device != device:
+        raise ValueError(f"{what} must be on {device} (got {t.device})")
+
+
+def _check_clip_state(clip, what: str = "clip"):
+    """A clip state is the tensor global_grad_norm returned (or a raw device
+    address, passed through unchecked for callers that manage their own)."""
+    if clip is None or isinstance(clip, int):
+        return
+    if not isinstance(clip, torch.Tensor):
+        raise TypeError(f"{what} must be the state tensor global_grad_norm returned or a device address")
+    if not clip.is_cuda or clip.dtype != torch.float32 or clip.numel() < 4 or not clip.is_contiguous():
+        raise ValueError(f"{what} must be a contiguous float32 GPU tensor of 4 entries")
+
+
 def _stream_handle(stream, device) -> int:
     if stream is None:
         stream = torch.cuda.current_stream(device)
@@ -189,6 +207,7 @@ def muon_hparams(beta=0.95, nesterov=True, ns_steps=5, ns_coeffs=NS_COEFFS, ns_e
                  clip=None) -> MuonHParamsC:
     """``ns_table``: one (a, b, c) per iteration (ns_steps rows), or None.
     ``clip``: the device state tensor global_grad_norm wrote, or None."""
+    _check_clip_state(clip)
     a, b, c = ns_coeffs
     h = MuonHParamsC()
     h.beta, h.normuon_beta2 = beta, normuon_beta2
@@ -233,8 +252,10 @@ def _muon_descs(tensors: Sequence[MuonParam], check_device=True):
         d.lr, d.weight_decay = t.lr, t.weight_decay
         if t.grad is not None:
             _check_dense(t.grad, f"muon[{i}].grad")
-            if t.grad.shape != p.shape or (check_device and t.grad.device != p.device):
-                raise ValueError(f"muon[{i}].grad must match param's shape and device")
+            if t.grad.shape != p.shape:
+                raise ValueError(f"muon[{i}].grad must match param's shape")
+            if check_device:
+                _check_device(t.grad, p.device, f"muon[{i}].grad")
             d.grad = t.grad.data_ptr()
             d.grad_dtype = _dtype_code(t.grad)
         else:
@@ -244,11 +265,15 @@ def _muon_descs(tensors: Sequence[MuonParam], check_device=True):
         _check_dense(m, f"muon[{i}].momentum")
         if m.dtype != torch.float32 or m.numel() != p.numel():
             raise ValueError(f"muon[{i}].momentum must be float32 with param's numel")
+        if check_device:
+            _check_device(m, p.device, f"muon[{i}].momentum")
         d.momentum = m.data_ptr()
         if t.row_v is not None:
             _check_dense(t.row_v, f"muon[{i}].row_v")
             if t.row_v.dtype != torch.float32 or t.row_v.numel() != batch * rows:
                 raise ValueError(f"muon[{i}].row_v must be float32 with batch*rows entries")
+            if check_device:
+                _check_device(t.row_v, p.device, f"muon[{i}].row_v")
             d.row_v = t.row_v.data_ptr()
         else:
             d.row_v = None
@@ -272,6 +297,8 @@ def muon_step(tensors: Sequence[MuonParam], hp: MuonHParamsC, workspace: Optiona
     need = lib.ma_muon_workspace_bytes(arr, len(tensors), ctypes.byref(hp))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=device or "cuda")
+    elif device is not None:
+        _check_device(workspace, device, "workspace")
     _check(lib.muon_step(arr, len(tensors), ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                          workspace.numel(), ctypes.c_void_p(_stream_handle(stream, workspace.device))))
     return workspace
@@ -291,6 +318,8 @@ def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, s
         if not t.param.is_cuda:
             raise ValueError(f"adamw[{i}].param must be on a GPU")
         device = device or t.param.device
+        for nm in ("param", "m", "v"):
+            _check_device(getattr(t, nm), device, f"adamw[{i}].{nm}")
         n = t.param.numel()
         if t.m.dtype != t.v.dtype or t.m.numel() != n or t.v.numel() != n:
             raise ValueError(f"adamw[{i}]: m and v must share a dtype and have param's numel")
@@ -302,10 +331,12 @@ def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, s
             _check_dense(t.grad, f"adamw[{i}].grad")
             if t.grad.numel() != n:
                 raise ValueError(f"adamw[{i}].grad must match param's numel")
+            _check_device(t.grad, device, f"adamw[{i}].grad")
             d.grad, d.grad_dtype = t.grad.data_ptr(), _dtype_code(t.grad)
         else:
             d.grad, d.grad_dtype = None, d.param_dtype
         d.lr, d.weight_decay = t.lr, t.weight_decay
+    _check_clip_state(clip)
     hp = AdamWHParamsC(beta1, beta2, eps, int(step))
     hp.cautious = CAUTIOUS["wrapper"] if cautious else 0
     hp.seed = int(seed) & ((1 << 64) - 1)
@@ -329,15 +360,20 @@ def global_grad_norm(grads: Sequence[Optional[torch.Tensor]], max_norm: float = 
         if not g.is_cuda:
             raise ValueError(f"grads[{i}] must be on a GPU")
         device = device or g.device
+        _check_device(g, device, f"grads[{i}]")
         arr[i].grad, arr[i].numel, arr[i].dtype = g.data_ptr(), g.numel(), _dtype_code(g)
     device = device or torch.device("cuda")
     if state is None:
         state = torch.empty(4, dtype=torch.float32, device=device)
+    else:
+        _check_clip_state(state, "state")
+        _check_device(state, device, "state")
     need = lib.ma_grad_norm_workspace_bytes(arr, len(grads))
     if need == 0:
         raise MuonAdamWError(1, lib.ma_last_error().decode())
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=device)
+    _check_device(workspace, device, "workspace")
     _check(lib.ma_global_grad_norm(arr, len(grads), float(max_norm), ctypes.c_void_p(state.data_ptr()),
                                    ctypes.c_void_p(workspace.data_ptr()), workspace.numel(),
                                    ctypes.c_void_p(_stream_handle(stream, device))))
@@ -352,14 +388,23 @@ def newton_schulz(x: torch.Tensor, hp: Optional[MuonHParamsC] = None, out: Optio
     _check_dense(x, "x")
     if not x.is_cuda:
         raise ValueError("x must be on a GPU")
+    if x.dim() not in (2, 3):
+        raise ValueError(f"x must be 2-D or 3-D, got {tuple(x.shape)}")
     batch, rows, cols = (1, *x.shape) if x.dim() == 2 else tuple(x.shape)
     dt = _dtype_code(x)
-    out = torch.empty_like(x) if out is None else out
+    if out is None:
+        out = torch.empty_like(x)
+    else:
+        _check_dense(out, "out")
+        if out.shape != x.shape or out.dtype != x.dtype:
+            raise ValueError("out must have x's shape and dtype")
+        _check_device(out, x.device, "out")
     need = lib.ma_newton_schulz_workspace_bytes(batch, rows, cols, dt, ctypes.byref(hp))
     if need == 0:
         raise MuonAdamWError(1, lib.ma_last_error().decode())
     if workspace is None or workspace.numel() < need:
         workspace = torch.empty(need, dtype=torch.uint8, device=x.device)
+    _check_device(workspace, x.device, "workspace")
     _check(lib.ma_newton_schulz(ctypes.c_void_p(x.data_ptr()), ctypes.c_void_p(out.data_ptr()), batch, rows,
                                 cols, dt, ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                                 workspace.numel(), ctypes.c_void_p(_stream_handle(stream, x.device))))

@@ -10,6 +10,7 @@ import re
 import subprocess
 
 import pytest
+import torch
 
 import muon_adamw_amd as ma
 import workloads
@@ -326,3 +327,18 @@ def test_newton_schulz_workspace_query(lib):
     assert lib.ma_newton_schulz_workspace_bytes(1, 300, 200, ma.MA_BF16, ctypes.byref(hp)) > 0
     assert lib.ma_newton_schulz_workspace_bytes(1, 0, 200, ma.MA_BF16, ctypes.byref(hp)) == 0
     assert lib.ma_newton_schulz(None, None, 1, 4, 4, ma.MA_F32, ctypes.byref(hp), None, 0, None) == 1
+
+
+def test_binding_rejects_host_memory_for_device_pointers():
+    """The binding checks that every tensor of a call lives on the call's GPU
+    before a pointer reaches the library (a host pointer would be dereferenced
+    by a kernel): the device helper and the clip-state check, on the host."""
+    t = torch.zeros(4)
+    with pytest.raises(ValueError, match="must be on cuda:0"):
+        ma._check_device(t, torch.device("cuda", 0), "momentum")
+    ma._check_device(t, torch.device("cpu"), "momentum")   # same device: accepted
+    with pytest.raises(ValueError, match="float32 GPU tensor"):
+        ma.muon_hparams(clip=torch.zeros(4))               # a host tensor as the clip state
+    with pytest.raises(TypeError):
+        ma.muon_hparams(clip="state")
+    assert ma.muon_hparams(clip=BASE).clip == BASE         # a raw device address passes through
