@@ -130,7 +130,7 @@ def check_momentum(gpu_mom, want_f32, tol=1e-5):
     assert rel(got, want_f32.astype(np.float64).ravel()) < tol
 
 
-def test_config1_end_to_end():
+def test_single_256x128_f32_end_to_end():
     """One fp32 256x128 tall matrix, fp32 Newton-Schulz: parameters, momentum
     and the orthogonalised update all within 1e-5 of the fp64 oracle."""
     wl = workloads.workload(1)
@@ -251,18 +251,18 @@ def run_and_check_muon(k, matrix_filter=None, oracle_filter=None, tol_ns=2e-2):
     return data, ws
 
 
-def test_config2_muon_full():
+def test_gpt_12L_d768_muon_full():
     """GPT 12L d768: all 72 matrices against the oracle."""
     run_and_check_muon(2)
 
 
-def test_config2_adamw():
+def test_gpt_12L_d768_adamw():
     wl = workloads.workload(2)
     data = to_gpu(workloads.generate(wl, device="cpu"))
     before = [(workloads.to_numpy(t.param), workloads.to_numpy(t.grad), workloads.to_numpy(t.m),
                workloads.to_numpy(t.v)) for t in data.adamw]
     h = wl.adamw_hp
-    flush("config2 adamw_step")
+    flush("gpt_12L_d768 adamw_step")
     ma.adamw_step(adamw_params(data), h.beta1, h.beta2, h.eps, h.step)
     torch.cuda.synchronize()
     tens = [{"param": p, "param_dtype": t.spec.param_dtype, "grad": g, "grad_dtype": t.spec.grad_dtype,
@@ -302,7 +302,7 @@ def test_adamw_two_steps_bf16_params_and_tail():
     assert np.abs(bits - storage.round_bf16_bits(p2).astype(np.int32)).max() <= 1
 
 
-def test_config4_sampled():
+def test_moe_64x2048_sampled():
     """MoE 64 experts: NorMuon + cautious weight-decay mask. Every matrix's
     momentum; the oracle's whole chain on a sample of gate, up and down
     matrices."""
@@ -310,7 +310,7 @@ def test_config4_sampled():
     run_and_check_muon(4, oracle_filter=lambda kk, info: kk in sample)
 
 
-def test_config3_sampled():
+def test_llama_8L_d4096_sampled():
     """Llama 8L d4096 (bf16 parameters, 1% gradient outliers), the full step in
     the bench's launch configuration: momentum of layer 0's q, k and both
     gate_up views; the oracle's whole chain on q (4096x4096), k (1024x4096)
@@ -319,7 +319,7 @@ def test_config3_sampled():
                        oracle_filter=lambda kk, info: info["view"] == 0)
 
 
-def test_config5_sampled():
+def test_wide_4L_d8192_sampled():
     """4L d8192 (bf16, Muon+ row_col and the cautious wrapper), the full step
     in the bench's launch configuration: momentum of layer 0's q and k, the
     oracle's whole chain on k (8192x8192; an 8192x28672 matrix takes the fp64
