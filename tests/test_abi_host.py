@@ -342,3 +342,44 @@ def test_binding_rejects_host_memory_for_device_pointers():
     with pytest.raises(TypeError):
         ma.muon_hparams(clip="state")
     assert ma.muon_hparams(clip=BASE).clip == BASE         # a raw device address passes through
+
+
+def one_desc(batch, rows, cols, views=1, dt=ma.MA_F32):
+    """A single fake descriptor (addresses only, nothing is dereferenced)."""
+    arr = (ma.MuonTensorC * 1)()
+    d = arr[0]
+    es = 2 if dt == ma.MA_BF16 else 4
+    n = batch * rows * cols
+    d.param = BASE
+    d.grad = BASE + n * es + (1 << 30)
+    d.momentum = BASE + 2 * (n * es + (1 << 30))
+    d.row_v = None
+    d.batch, d.rows, d.cols, d.views = batch, rows, cols, views
+    d.param_dtype = d.grad_dtype = dt
+    d.lr, d.weight_decay = 0.02, 0.1
+    return arr
+
+
+def test_size_limits_and_degenerate_descriptors(lib):
+    """Extents the planner refuses before touching the GPU: empty or negative
+    extents, misaligned parameters, a negative tensor count (invalid, 1); one
+    dimension above 65536, too many matrices in one tensor, a padded matrix
+    above 2^31 elements (unsupported, 5). The largest accepted extents plan."""
+    hp = ma.muon_hparams()
+    ok = one_desc(1, 300, 200)
+    assert counts(lib, ok, 1, hp)[1:] == (1, 1)
+    for b, r, c in [(0, 4, 4), (1, 0, 4), (1, 4, 0), (-1, 4, 4)]:
+        assert step(lib, one_desc(b, r, c), 1, hp) == 1, (b, r, c)
+    arr = one_desc(1, 8, 8); arr[0].param = BASE + 2          # fp32 param not 4-byte aligned
+    assert step(lib, arr, 1, hp) == 1
+    assert lib.muon_step(ok, -1, ctypes.byref(hp), None, 0, None) == 1
+    assert step(lib, one_desc(1, 65537, 8), 1, hp) == 5
+    assert step(lib, one_desc(1, 8, 65537), 1, hp) == 5
+    assert b"65536" in lib.ma_last_error()
+    assert step(lib, one_desc((1 << 20) + 1, 4, 4), 1, hp) == 5
+    assert step(lib, one_desc(1, 65536, 65536), 1, hp) == 5   # padded 2^32 elements
+    assert b"too large" in lib.ma_last_error()
+    # views split the rows: 2 x 65536 rows is two matrices of the largest accepted height
+    big = one_desc(1, 2 * 65536, 1024, views=2)
+    assert counts(lib, big, 1, hp)[1:] == (2, 1)
+    assert lib.ma_muon_workspace_bytes(big, 1, ctypes.byref(hp)) > 0
