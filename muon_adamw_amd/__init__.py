@@ -362,7 +362,8 @@ def global_grad_norm(grads: Sequence[Optional[torch.Tensor]], max_norm: float = 
         device = device or g.device
         _check_device(g, device, f"grads[{i}]")
         arr[i].grad, arr[i].numel, arr[i].dtype = g.data_ptr(), g.numel(), _dtype_code(g)
-    device = device or torch.device("cuda")
+    # with every gradient absent, the current GPU (with its index, as tensors report it)
+    device = device or torch.device("cuda", torch.cuda.current_device())
     if state is None:
         state = torch.empty(4, dtype=torch.float32, device=device)
     else:

@@ -50,3 +50,12 @@ def test_grad_norm_state_and_newton_schulz_out_are_checked():
         ma.newton_schulz(torch.zeros(8, device=DEV))
     with pytest.raises(ValueError, match="workspace"):
         ma.newton_schulz(x, workspace=torch.zeros(1 << 24, dtype=torch.uint8))
+
+
+def test_grad_norm_with_every_gradient_absent():
+    """No gradient at all is a valid call: the binding defaults to the current
+    GPU, and the state reads norm 0, clip factor 1, no skip."""
+    state = ma.global_grad_norm([None, None], 1.0)
+    torch.cuda.synchronize()
+    assert state.device.type == "cuda"
+    assert state.cpu().tolist()[:3] == [0.0, 1.0, 0.0]
