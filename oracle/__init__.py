@@ -14,13 +14,17 @@ primitive used):
 * ``muon``  -- momentum EMA, Nesterov lerp, Frobenius normalisation, the quintic
   Newton-Schulz iteration with tall matrices transposed, the shape scale, the
   decoupled weight decay, NorMuon, Muon+ row_col, and both cautious forms.
-* ``adamw`` -- decoupled-weight-decay Adam with bias correction.
-* ``storage`` -- the storage formats: decoding bf16 bit patterns and rounding
-  float64 results to float32 / bf16 with round-to-nearest-even.
+* ``adamw`` -- decoupled-weight-decay Adam with bias correction, the cautious
+  wrapper, and bf16 moments (widened for the update, written back through
+  ``storage``'s stochastic rounding).
+* ``gradnorm`` -- the global gradient norm, the clip factor and the skip flag.
+* ``storage`` -- the storage formats: decoding bf16 bit patterns, rounding
+  float64 results to float32 / bf16 with round-to-nearest-even, and stochastic
+  rounding to bf16 with a SplitMix64 counter hash.
 
 Parity status: every function here is pinned by the ``-m "not gpu"`` tests in
 ``tests/test_oracle_pins.py`` (closed forms, the SVD reduction of
 Newton-Schulz, invariants, brute force on tiny inputs) except where a docstring
 says "parity unpinned".
 """
-from . import storage, muon, adamw  # noqa: F401
+from . import storage, muon, adamw, gradnorm  # noqa: F401
