@@ -8,6 +8,7 @@ import math
 import os
 import re
 import subprocess
+import sys
 
 import pytest
 import torch
@@ -383,3 +384,18 @@ def test_size_limits_and_degenerate_descriptors(lib):
     big = one_desc(1, 2 * 65536, 1024, views=2)
     assert counts(lib, big, 1, hp)[1:] == (2, 1)
     assert lib.ma_muon_workspace_bytes(big, 1, ctypes.byref(hp)) > 0
+
+
+def test_missing_library_fails_loudly(tmp_path):
+    """No CPU fallback: loading a library that is not there raises ImportError
+    (every entry point of the binding loads the library first). Checked in a
+    fresh interpreter, since the binding caches the library once loaded."""
+    code = ("import muon_adamw_amd as ma\n"
+            f"ma.LIB_PATH = {str(tmp_path / 'missing.so')!r}\n"
+            "try:\n"
+            "    ma.load_library(ma.LIB_PATH)\n"
+            "except ImportError as e:\n"
+            "    print('ImportError', e)\n")
+    r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
+    assert r.returncode == 0, r.stderr
+    assert "ImportError" in r.stdout and "missing.so" in r.stdout
