@@ -379,6 +379,28 @@ def test_adamw_zero_grad_is_pure_decay():
     assert np.allclose(p1, p * (1 - 1e-4), rtol=0, atol=1e-18)
 
 
+def test_adamw_matches_torch_optim_adamw():
+    """Four steps of the oracle against torch.optim.AdamW in float64 on the CPU
+    (decoupled decay, bias-corrected moments, eps outside the square root), a
+    library routine the oracle shares no code with."""
+    r = np.random.default_rng(21)
+    p = r.standard_normal(257)
+    lr, wd, b1, b2, eps = 3e-3, 0.1, 0.9, 0.95, 1e-8
+    tp = torch.nn.Parameter(torch.from_numpy(p.copy()))
+    opt = torch.optim.AdamW([tp], lr=lr, betas=(b1, b2), eps=eps, weight_decay=wd)
+    m = np.zeros_like(p)
+    v = np.zeros_like(p)
+    for step in range(1, 5):
+        g = r.standard_normal(257) * 10.0 ** r.integers(-3, 3)
+        tp.grad = torch.from_numpy(g.copy())
+        opt.step()
+        p, m, v = oadamw.adamw_update(p, g, m, v, lr, wd, b1, b2, eps, step)
+        st = opt.state[tp]
+        assert np.abs(m - st["exp_avg"].numpy()).max() <= 1e-15 * np.abs(m).max()
+        assert np.abs(v - st["exp_avg_sq"].numpy()).max() <= 1e-15 * np.abs(v).max()
+        assert np.abs(p - tp.detach().numpy()).max() <= 1e-14 * np.abs(p).max()
+
+
 # ---------------------------------------------------------------------------
 # Storage formats
 # ---------------------------------------------------------------------------
