@@ -568,6 +568,27 @@ def test_global_norm_and_clip_closed_forms():
     assert ognorm.clip_state(ognorm.global_norm([(nan, "f32")]), 0.0)[1] is True
 
 
+def test_global_norm_matches_torch_clip_grad_norm():
+    """The norm over several fp32 and bf16 gradients against
+    torch.nn.utils.clip_grad_norm_ in float64 on the decoded values, and the
+    scaled gradients against torch's (whose factor has 1e-6 added to the norm)."""
+    r = np.random.default_rng(22)
+    stored = [(r.standard_normal(1000).astype(np.float32), "f32"),
+              (storage.round_bf16_bits(r.standard_normal((33, 7)) * 3.0), "bf16"),
+              (r.standard_normal(5).astype(np.float32) * 100.0, "f32")]
+    nrm = ognorm.global_norm(stored + [None])
+    ts = [torch.nn.Parameter(torch.zeros(storage.decode(x, dt).size, dtype=torch.float64)) for x, dt in stored]
+    for t, (x, dt) in zip(ts, stored):
+        t.grad = torch.from_numpy(storage.decode(x, dt).reshape(-1).astype(np.float64))
+    ref = float(torch.nn.utils.clip_grad_norm_(ts, max_norm=50.0))
+    assert abs(nrm - ref) <= 1e-15 * ref
+    factor, skip = ognorm.clip_state(nrm, 50.0)
+    assert not skip and factor < 1.0
+    for t, (x, dt) in zip(ts, stored):
+        want = storage.decode(x, dt).reshape(-1) * factor
+        assert np.abs(t.grad.numpy() - want).max() <= 1e-7 * np.abs(want).max()
+
+
 def test_clip_skip_leaves_every_buffer_and_scales_the_gradient():
     """A skipped step returns every stored input unchanged (both halves); a
     clip factor enters as a scaled gradient: from zero momentum the new
