@@ -166,6 +166,39 @@ def test_second_step_closed_form():
     check_second_step()
 
 
+def test_muon_steps_match_torch_optim_muon():
+    """Three steps of the oracle's plain Muon on a wide and a tall matrix against
+    torch.optim.Muon in float64, with torch's Newton-Schulz call (bf16, and a
+    clamped norm instead of norm + eps) swapped for the SVD closed form of the
+    quintic iteration: the momentum, the Nesterov lerp, the shape scale and the
+    decoupled decay then come from the library."""
+    import torch.optim._muon as tmuon
+    r = rng(23)
+    shapes = [(48, 80), (96, 32)]
+    lr, wd = 0.02, 0.1
+    Ws = [0.02 * r.standard_normal(s) for s in shapes]
+    Bs = [np.zeros((1,) + s) for s in shapes]
+    tps = [torch.nn.Parameter(torch.from_numpy(W.copy())) for W in Ws]
+    orig = tmuon._zeropower_via_newtonschulz
+    tmuon._zeropower_via_newtonschulz = lambda g, coeffs, steps, eps: torch.from_numpy(
+        ns_by_svd(g.numpy(), steps, eps))
+    try:
+        opt = torch.optim.Muon(tps, lr=lr, weight_decay=wd, momentum=0.95, nesterov=True, ns_steps=STEPS,
+                               eps=EPS)
+        for _ in range(3):
+            Gs = [r.standard_normal(s) for s in shapes]
+            for tp, G in zip(tps, Gs):
+                tp.grad = torch.from_numpy(G.copy())
+            opt.step()
+            for k, G in enumerate(Gs):
+                W1, B1, _, _ = omuon.muon_tensor_step(Ws[k][None], G[None], Bs[k], None, 1, HP, lr, wd)
+                Ws[k], Bs[k] = W1[0], B1
+                assert np.abs(Ws[k] - tps[k].detach().numpy()).max() < 1e-13
+                assert np.abs(Bs[k][0] - opt.state[tps[k]]["momentum_buffer"].numpy()).max() < 1e-15
+    finally:
+        tmuon._zeropower_via_newtonschulz = orig
+
+
 def test_nesterov_off_uses_momentum():
     r = rng(2)
     G = r.standard_normal((1, 8, 12))
