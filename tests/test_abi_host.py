@@ -10,11 +10,13 @@ import re
 import subprocess
 import sys
 
+import numpy as np
 import pytest
 import torch
 
 import muon_adamw_amd as ma
 import workloads
+from oracle import muon as omuon
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "muon_adamw.h")
@@ -399,3 +401,47 @@ def test_missing_library_fails_loudly(tmp_path):
     r = subprocess.run([sys.executable, "-c", code], capture_output=True, text=True, cwd=ROOT)
     assert r.returncode == 0, r.stderr
     assert "ImportError" in r.stdout and "missing.so" in r.stdout
+
+
+def test_matrix_expansion_matches_the_oracle_on_random_lists(lib):
+    """Random tensor lists (batches, packed views, tall, wide, ragged, absent
+    gradients): the planner's matrices, in order, against the oracle's expansion
+    (tensor, then batch entry, then view; rows / views x cols each), with the
+    canonical shape, the 128-padding, the orientation, the oracle's shape scale
+    and first-appearance shape buckets."""
+    r = np.random.default_rng(31)
+    for trial in range(20):
+        n = int(r.integers(1, 7))
+        arr = (ma.MuonTensorC * n)()
+        addr, expect = BASE, []
+        for i in range(n):
+            views = int(r.choice([1, 1, 2, 3]))
+            m = int(r.choice([1, 7, 64, 128, 129, 300, 768, 1000]))
+            cols = int(r.choice([1, 5, 128, 200, 768, 3072]))
+            batch = int(r.choice([1, 1, 2, 4]))
+            d = arr[i]
+            numel = batch * m * views * cols
+            d.param = addr; addr += 4 * numel + (1 << 30)
+            d.grad = addr if r.random() > 0.2 else None
+            addr += 4 * numel + (1 << 30)
+            d.momentum = addr; addr += 4 * numel + (1 << 30)
+            d.row_v = None
+            d.batch, d.rows, d.cols, d.views = batch, m * views, cols, views
+            d.param_dtype = d.grad_dtype = ma.MA_F32
+            d.lr, d.weight_decay = 0.02, 0.1
+            if d.grad:
+                expect += [(i, b, v, m, cols) for b in range(batch) for v in range(views)]
+        hp = ma.muon_hparams()
+        st, nm, nb = counts(lib, arr, n, hp)
+        assert st == 0, lib.ma_last_error()
+        assert nm == len(expect)
+        buckets = {}
+        for k, (i, b, v, m, cols) in enumerate(expect):
+            mi = info(lib, arr, n, hp, k)
+            rr, cc = min(m, cols), max(m, cols)
+            assert (mi.tensor, mi.batch_index, mi.view, mi.m, mi.n) == (i, b, v, m, cols)
+            assert (mi.r, mi.c, mi.rp, mi.cp) == (rr, cc, -(-rr // 128) * 128, -(-cc // 128) * 128)
+            assert mi.transposed == int(m > cols)
+            assert mi.scale == pytest.approx(omuon.shape_scale(m, cols), rel=1e-7)
+            assert mi.bucket == buckets.setdefault((rr, cc), len(buckets))
+        assert nb == len(buckets)
