@@ -1,6 +1,7 @@
-"""bench.py's contract on a host without a GPU: more than one GPU is refused
-with a message (this build runs on one GPU), and without a visible GPU the
-bench fails loudly instead of falling back to anything."""
+"""bench.py on a host without a GPU: more than one GPU is refused with a
+message (this build runs on one GPU), without a visible GPU the bench fails
+loudly instead of falling back to anything, and its algorithmic units and
+cpu_baseline leg give the figures the roofline and the baseline report."""
 import os
 import subprocess
 import sys
@@ -29,3 +30,36 @@ def test_no_gpu_fails_loudly():
     assert r.returncode != 0
     assert "no GPU" in r.stderr
     assert r.stdout.strip() == ""
+
+
+def test_algorithmic_units():
+    """The per-unit figures the roofline object divides by: Newton-Schulz FLOPs
+    per matrix and iteration (one triangle for the Gram and the square, as
+    computed) and the elementwise bytes per element (14 B momentum, 10 B apply,
+    28 B AdamW for fp32 with bf16 Newton-Schulz buffers) on the d768 set."""
+    import bench
+    import workloads
+    r, c = 256, 768
+    assert bench.ns_flops(r, c, 1) == r * (r + 1) * c + r * (r + 1) * r + 2 * r * r * c
+    assert bench.ns_flops(r, c, 5) == 5 * bench.ns_flops(r, c, 1)
+    per = bench.ns_flops_per_launch([(r, c), (c, c)])
+    assert per["ns_gram_bf16"] + per["ns_square_bf16"] + per["ns_apply_bf16"] == \
+        bench.ns_flops_persistent([(r, c), (c, c)], 1)
+    wl = workloads.workload(2)
+    muon = sum(t.numel for t in wl.muon if t.has_grad)
+    adam = sum(t.numel for t in wl.adamw)
+    b = bench.elementwise_bytes(wl)
+    assert b == {"momentum": 14 * muon, "apply_update": 10 * muon, "adamw": 28 * adam}
+    assert abs(b["momentum"] / 1e9 - 1.19) < 0.01 and abs(b["adamw"] / 1e9 - 1.08) < 0.01
+
+
+def test_cpu_baseline_times_the_oracle():
+    """The cpu_baseline leg on the small single-matrix set, on the host: the
+    oracle timed on a bounded sample, reported in the GPU figure's unit."""
+    import bench
+    import workloads
+    wl = workloads.workload(1)
+    out = bench.cpu_baseline(wl, workloads.generate(wl, device="cpu"), 0.0)
+    assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
+    assert out["value"] > 0 and out["cores"] >= 1
+    assert out["sample"].startswith("full fp64 Muon update of 1 of 1 matrices")
