@@ -323,6 +323,8 @@ def _sr_no_nan_rule(x32, key, index0=0):
     return ((u + r) >> np.uint64(16)).astype(np.uint16).reshape(x32.shape)
 
 
+# the mutant without the NaN rule hands NaN on as bits; decoding them warns
+@pytest.mark.filterwarnings("ignore::RuntimeWarning")
 @pytest.mark.parametrize("mutant", [_sr_wide_noise, _sr_no_nan_rule], ids=lambda f: f.__name__)
 def test_stochastic_rounding_mutants_caught(mutant, monkeypatch):
     monkeypatch.setattr(ostorage, "stochastic_round_bf16_bits", mutant)
