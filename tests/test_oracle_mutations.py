@@ -375,3 +375,51 @@ def test_ns_table_reversed_caught(monkeypatch):
     monkeypatch.setattr(omuon, "newton_schulz", reversed_table)
     with pytest.raises(AssertionError):
         pins.test_ns_table_closed_forms_and_order()
+
+
+# -- the wide-model composition: Newton-Schulz -> Muon+ -> scale -> wrapper on G --
+def _wrapper_fed_nesterov_q(W, G, Bm, V, views, hp, lr, wd):
+    """The wrapper's mask taken against the Nesterov Q instead of the raw gradient."""
+    beta = hp.get("beta", 0.95)
+    B_new = omuon.momentum_ema(Bm, G, beta)
+    Q = omuon.nesterov_lerp(G, B_new, beta)
+    m = W.shape[1] // views
+    Wn = np.empty_like(W)
+    for b in range(W.shape[0]):
+        for v in range(views):
+            sl = slice(v * m, (v + 1) * m)
+            Wn[b, sl], _, _ = omuon.matrix_update(Q[b, sl], W[b, sl], Q[b, sl], None, hp, lr, wd)
+    return Wn, B_new, None, None
+
+
+def _muon_plus_after_scale(Q, W, G, V, hp, lr, wd):
+    """Muon+ applied to s*U: the normalisation then removes the shape scale."""
+    m, n = Q.shape
+    s = omuon.shape_scale(m, n)
+    U = omuon.newton_schulz(Q)
+    U_dir = omuon.muon_plus_row_col(s * U, hp.get("muon_plus_eps", 1e-8))
+    W_new, _ = omuon.apply_cautious_wrapper(W, U_dir, G, lr, wd, 1.0)
+    return W_new, V, U
+
+
+def _mask_before_muon_plus(Q, W, G, V, hp, lr, wd):
+    """The wrapper's mask decided on the Newton-Schulz output before Muon+."""
+    m, n = Q.shape
+    s = omuon.shape_scale(m, n)
+    U = omuon.newton_schulz(Q)
+    U_dir = omuon.muon_plus_row_col(U, hp.get("muon_plus_eps", 1e-8))
+    delta = lr * wd * W + lr * s * U_dir
+    mask = (lr * wd * W + lr * s * U) * G > 0.0
+    return np.where(mask, W - delta, W), V, U
+
+
+def test_wrapper_fed_nesterov_q_caught():
+    with pytest.raises(AssertionError):
+        pins.check_muon_plus_wrapper_step(_wrapper_fed_nesterov_q)
+
+
+@pytest.mark.parametrize("mutant", [_muon_plus_after_scale, _mask_before_muon_plus], ids=lambda f: f.__name__)
+def test_muon_plus_composition_mutants_caught(mutant, monkeypatch):
+    monkeypatch.setattr(omuon, "matrix_update", mutant)
+    with pytest.raises(AssertionError):
+        pins.check_muon_plus_wrapper_step()

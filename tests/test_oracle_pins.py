@@ -374,6 +374,64 @@ def test_step_with_normuon_and_cautious_wd():
             assert np.abs(W1[b, sl] - want).max() < 1e-14
 
 
+def _row_col_by_diagonals(U, eps):
+    """Muon+ row_col written as two diagonal scalings, D_r^-1 U D_c^-1: D_r
+    from the rows of U, D_c from the columns of the row-normalised matrix
+    (speedtronic "v2 optimizers", "Muon+": rows first, then columns, eps
+    inside each square root)."""
+    d_r = np.array([math.sqrt(float(U[i] @ U[i]) + eps) for i in range(U.shape[0])])
+    R = np.diag(1.0 / d_r) @ U
+    d_c = np.array([math.sqrt(float(R[:, j] @ R[:, j]) + eps) for j in range(U.shape[1])])
+    return R @ np.diag(1.0 / d_c)
+
+
+def check_muon_plus_wrapper_step(step_fn=None):
+    """The wide-model workload's whole composition over two steps: Newton-Schulz
+    (by SVD), then Muon+ row_col, then the shape scale, then
+    delta = lr*wd*W + lr*s*U, kept only where delta * G > 0 with G this step's
+    raw gradient (speedtronic "v2 optimizers": "Muon update", "Muon+",
+    "Cautious updates"). A packed tensor of two tall 12x5 views (scale
+    sqrt(12/5)) and a wide 5x12 tensor (scale 1). The second gradient is drawn
+    so that at some entries its sign differs from the Nesterov Q's, which a
+    mask taken from Q instead of G would get wrong."""
+    step_fn = step_fn or omuon.muon_tensor_step
+    r = rng(31)
+    lr, wd, eps = 0.02, 0.1, 1e-8
+    hp = dict(HP, muon_plus=True, muon_plus_eps=eps, cautious="wrapper")
+    for views, m, n in [(2, 12, 5), (1, 5, 12)]:
+        s = math.sqrt(max(1.0, m / n))
+        shape = (1, views * m, n)
+        G1 = r.standard_normal(shape)
+        # G2 opposes 3*G1 in a quarter of the entries: there Q2 = 0.045125 G1 +
+        # 0.0975 G2 takes G1's sign, against G2's
+        G2 = r.standard_normal(shape)
+        flip = r.random(shape) < 0.25
+        G2[flip] = -0.3 * G1[flip]
+        W0 = 0.02 * r.standard_normal(shape)
+        Q1 = 0.0975 * G1
+        Q2 = 0.045125 * G1 + 0.0975 * G2
+        assert np.any(np.sign(Q2) != np.sign(G2))
+        W1, B1, _, _ = step_fn(W0, G1, np.zeros(shape), None, views, hp, lr, wd)
+        W2, B2, _, _ = step_fn(W1, G2, B1, None, views, hp, lr, wd)
+        assert np.abs(B2 - (0.0475 * G1 + 0.05 * G2)).max() < 1e-15
+        masks_differ = 0
+        for (Wprev, Wgot, Q, G) in [(W0, W1, Q1, G1), (W1, W2, Q2, G2)]:
+            for v in range(views):
+                sl = slice(v * m, (v + 1) * m)
+                U = _row_col_by_diagonals(ns_by_svd(Q[0, sl]), eps)
+                delta = lr * wd * Wprev[0, sl] + lr * s * U
+                prod = delta * G[0, sl]
+                assert np.abs(prod).min() > 1e-12          # no tie near the decision
+                want = np.where(prod > 0, Wprev[0, sl] - delta, Wprev[0, sl])
+                assert np.abs(Wgot[0, sl] - want).max() < 1e-14, (views, m, n, v)
+                masks_differ += int(np.sum((prod > 0) != (delta * Q[0, sl] > 0)))
+        assert masks_differ > 0
+
+
+def test_muon_plus_and_wrapper_two_steps():
+    check_muon_plus_wrapper_step()
+
+
 # ---------------------------------------------------------------------------
 # AdamW closed forms
 # ---------------------------------------------------------------------------
