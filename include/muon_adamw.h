@@ -16,10 +16,16 @@
  * failure seen right after enqueueing returns MA_E_HIP.
  *
  * Streams: `stream` is a hipStream_t (NULL = the legacy default stream). All
- * work of one call is enqueued on that stream in order; no call synchronises
- * the host with the device except the staging ring's reuse wait (an event from
- * four calls earlier). Calls that share a workspace must be ordered on one
- * stream.
+ * work of one call is enqueued on that stream in order. No call synchronises
+ * the host with the device, except ma_muon_step_status() and, when the host
+ * runs 64 calls ahead of the device, the reuse of a pinned staging buffer.
+ * Calls that share a workspace must be ordered on one stream.
+ *
+ * Plans: muon_step keeps the plan of a tensor list (its matrices, shape
+ * buckets, launch tables and workspace layout) keyed by the list's structure
+ * (which tensors have gradients, their batch, rows, cols and views), the
+ * Newton-Schulz dtype, step count and coefficients. A later call with the same
+ * structure skips the planning; arguments are still validated on every call.
  */
 #ifndef MUON_ADAMW_H
 #define MUON_ADAMW_H
@@ -165,9 +171,29 @@ size_t ma_muon_workspace_bytes(const ma_muon_tensor* tensors, int32_t n,
  * on entry do not matter. Enqueues: the fused momentum/Nesterov/norm pass,
  * ns_steps x (Gram, A^2 -> bA + cA^2, aX + BX) batched over all matrices,
  * the optional NorMuon / Muon+ reductions, and the fused scale/decay/apply.
+ * The first int32 of the workspace receives the call's device status (see
+ * ma_muon_step_status).
  */
 ma_status muon_step(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
                     void* workspace, size_t workspace_bytes, void* stream);
+
+/*
+ * Device status of the last muon_step or ma_newton_schulz that used
+ * `workspace` (device, 256-byte aligned) and had at least one matrix to
+ * step. Waits for `stream` (the stream of that call) and writes the status to
+ * host `*status`: 0 when the step ran to completion. The bits come from the
+ * persistent Newton-Schulz launch, which hands every XCD of the device a queue
+ * of tiles and bounds each of its waits:
+ *   MA_NS_WAIT_TIMEOUT     a wait for another tile ran out (about a second);
+ *                          the launch went on, so some results may have been
+ *                          computed from incomplete operands;
+ *   MA_NS_QUEUE_UNDRAINED  an XCD's queue was not handed out to its end, so
+ *                          some matrices were left unfinished.
+ * Either means the step's results are not to be used. A step skipped by the
+ * clip state reports 0. Returns MA_E_HIP if the read fails.
+ */
+enum { MA_NS_WAIT_TIMEOUT = 1, MA_NS_QUEUE_UNDRAINED = 2 };
+ma_status ma_muon_step_status(const void* workspace, int32_t* status, void* stream);
 
 /*
  * One tensor stepped by AdamW (dew.training.optim: optax.adamw; speedtronic
@@ -237,9 +263,10 @@ ma_status adamw_step(const ma_adamw_tensor* tensors, int32_t n, const ma_adamw_h
  *            or numel 0 contributes nothing). Pass the Muon and the AdamW
  *            gradients of the step together.
  * state      device, 4 floats, 16-byte aligned, written on the stream:
- *            [0] ||g||_2 over all elements (fp32 partial sums per 8192
+ *            [0] ||g||_2 over all elements (fp64 sums of squares per 8192
  *            elements, added in fp64 in a fixed order: the same bits for the
- *            same inputs), [1] the clip factor min(1, max_norm / ||g||) (1 when
+ *            same inputs, and no overflow for any finite gradient), [1] the
+ *            clip factor min(1, max_norm / ||g||) (1 when
  *            max_norm <= 0 or ||g|| <= max_norm), [2] 1 when ||g|| is not
  *            finite (the step is to be skipped), else 0, [3] 0.
  *            Hand `state` to muon_step and adamw_step (hparams.clip): they read

@@ -79,7 +79,9 @@ class KernelTimeC(ctypes.Structure):
 EXPORTS = ("muon_step", "adamw_step", "ma_muon_workspace_bytes", "ma_last_error",
            "ma_newton_schulz", "ma_newton_schulz_workspace_bytes", "ma_muon_plan_counts",
            "ma_muon_matrix_info", "ma_profile_begin", "ma_profile_end", "ma_grad_norm_workspace_bytes",
-           "ma_global_grad_norm")
+           "ma_global_grad_norm", "ma_muon_step_status")
+# bits of ma_muon_step_status
+NS_WAIT_TIMEOUT, NS_QUEUE_UNDRAINED = 1, 2
 
 _lib = None
 
@@ -119,6 +121,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_grad_norm_workspace_bytes.restype = SZ
     lib.ma_global_grad_norm.argtypes = [ctypes.POINTER(GradRefC), I32, ctypes.c_float, P, P, SZ, P]
     lib.ma_global_grad_norm.restype = ctypes.c_int
+    lib.ma_muon_step_status.argtypes = [P, ctypes.POINTER(I32), P]
+    lib.ma_muon_step_status.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -302,6 +306,20 @@ def muon_step(tensors: Sequence[MuonParam], hp: MuonHParamsC, workspace: Optiona
     _check(lib.muon_step(arr, len(tensors), ctypes.byref(hp), ctypes.c_void_p(workspace.data_ptr()),
                          workspace.numel(), ctypes.c_void_p(_stream_handle(stream, workspace.device))))
     return workspace
+
+
+def muon_step_status(workspace: torch.Tensor, stream=None) -> int:
+    """Device status of the last muon_step / newton_schulz that used
+    ``workspace``: 0 when it ran to completion, else NS_WAIT_TIMEOUT and/or
+    NS_QUEUE_UNDRAINED (its results are then not to be used). Waits for the
+    stream."""
+    lib = load_library()
+    if not workspace.is_cuda:
+        raise ValueError("workspace must be on a GPU")
+    st = ctypes.c_int32(-1)
+    _check(lib.ma_muon_step_status(ctypes.c_void_p(workspace.data_ptr()), ctypes.byref(st),
+                                   ctypes.c_void_p(_stream_handle(stream, workspace.device))))
+    return int(st.value)
 
 
 def adamw_step(tensors: Sequence[AdamWParam], beta1=0.9, beta2=0.95, eps=1e-8, step=1, stream=None,

@@ -15,6 +15,7 @@
 #include <cmath>
 #include <cstring>
 #include <map>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <cstdlib>
@@ -24,6 +25,9 @@
 #include "kernels.hpp"
 
 using namespace ma;
+
+static_assert(MA_NS_WAIT_TIMEOUT == NS_STATUS_WAIT_TIMEOUT && MA_NS_QUEUE_UNDRAINED == NS_STATUS_QUEUE_UNDRAINED,
+              "status bits of the header and the kernels");
 
 namespace {
 
@@ -35,6 +39,9 @@ ma_status fail(ma_status s, const std::string& msg) {
 }
 
 constexpr size_t kAlign = 256;
+// The first bytes of a Muon workspace: the status word of the call that last
+// used it (int32 at offset 0), then padding.
+constexpr size_t kHeaderBytes = 256;
 size_t align_up(size_t x, size_t a = kAlign) { return (x + a - 1) / a * a; }
 int64_t round_up(int64_t x, int64_t a) { return (x + a - 1) / a * a; }
 size_t dtype_size(int32_t dt) { return dt == MA_BF16 ? 2 : 4; }
@@ -68,10 +75,11 @@ struct Plan {
   std::vector<int32_t> ints;
   size_t desc_bytes = 0, table_bytes = 0, ws_bytes = 0;
   // persistent Newton-Schulz launch (bf16): per-XCD segment lists in `ints`
-  // (int4 records from byte segs_off) and a zeroed counter region
+  // (int4 records from byte segs_off) and a zeroed counter region; built
+  // whenever the launch could be used (a call still takes the per-launch
+  // schedule on a device that cannot run it, or when asked to)
   bool persist = false;
   size_t coefs_off = 0;   // byte offset of the coefficient table within the int tables
-  int operands = 0;   // 0: by size (k-major up to kKmajorMaxRows), 1: k-major, 2: row-wise
   size_t segs_off = 0, off_counters = 0;
   int counter_ints = 0;
   int32_t seg_off[8] = {0, 0, 0, 0, 0, 0, 0, 0};
@@ -89,7 +97,8 @@ constexpr int kXcds = 8;  // MI355X: 8 XCDs, workgroups dealt round-robin
 // Steps with at most this many matrices run Newton-Schulz as one persistent
 // launch; the counter region grows by 128 bytes per matrix. The environment
 // variable MA_NS_SCHEDULE=launches selects three launches per iteration
-// instead (same tiles, plain kernel boundaries between the products).
+// instead (same tiles, plain kernel boundaries between the products), and so
+// does a device that is not one MI355X of 8 XCDs.
 constexpr int kMaxPersistMats = 1 << 16;
 // SQUARE and APPLY of matrices with at most this many (padded) rows read
 // both operands k-major; larger ones read their symmetric operand row-wise.
@@ -196,16 +205,14 @@ ma_status check_overlaps(std::vector<Range>& rs) {
   return MA_OK;
 }
 
-// Validates the list and builds the plan. `ns_only`: the Newton-Schulz-only
-// entry (no momentum, param = output).
-ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* hp, bool ns_only, Plan& P) {
+// Validates every argument that a call brings: pointers, alignment, dtypes,
+// sizes, values and overlaps. Runs on every call. `ns_only`: the
+// Newton-Schulz-only entry (no momentum, param = output).
+ma_status validate_tensors(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* hp, bool ns_only) {
   ma_status st = validate_hparams(hp);
   if (st != MA_OK) return st;
   if (n < 0) return fail(MA_E_INVALID, "tensor count is negative");
   if (n > 0 && !t) return fail(MA_E_INVALID, "tensor array is NULL");
-  P = Plan();
-  P.ns_dt = hp->ns_dtype;
-  P.gemm_tile = hp->ns_dtype == MA_BF16 ? kNsTileBf16 : kNsTileF32;
   std::vector<Range> ranges;
   for (int i = 0; i < n; ++i) {
     const ma_muon_tensor& x = t[i];
@@ -243,6 +250,18 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     st = check_overlaps(ranges);
     if (st != MA_OK) return st;
   }
+  return MA_OK;
+}
+
+// Builds the plan of a validated list: the matrices, their buckets, the
+// launch tables and the workspace layout. It depends only on the list's
+// structure (which tensors have gradients, their shapes and views), the
+// Newton-Schulz dtype and step count and the coefficients, which is what
+// plan_key() below captures.
+ma_status structure_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* hp, Plan& P) {
+  P = Plan();
+  P.ns_dt = hp->ns_dtype;
+  P.gemm_tile = hp->ns_dtype == MA_BF16 ? kNsTileBf16 : kNsTileF32;
 
   // Expand into matrices, canonicalise, bucket.
   std::map<std::pair<int, int>, int> buckets;
@@ -328,12 +347,10 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     P.app = add_map(P, app, &xcd_of);
     // Queues of the persistent launch: per XCD, segments in (iteration,
     // product, matrix) order, matrices longest first; a segment needs every
-    // earlier product of its matrix complete.
-    const char* opnd = std::getenv("MA_NS_OPERANDS");
-    P.operands = opnd && std::string(opnd) == "kmajor" ? 1 : (opnd && std::string(opnd) == "rows" ? 2 : 0);
-    const char* sched = std::getenv("MA_NS_SCHEDULE");
-    const bool launches = sched && std::string(sched) == "launches";
-    if (nm <= kMaxPersistMats && !launches) {
+    // earlier product of its matrix complete. They are built whenever the
+    // launch could be used, so the workspace size does not depend on the
+    // device or on the schedule a call takes.
+    if (nm <= kMaxPersistMats) {
       P.persist = true;
       while (P.ints.size() % 4) P.ints.push_back(0);
       P.segs_off = P.ints.size() * sizeof(int32_t);
@@ -382,9 +399,11 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
       P.ints.push_back(bits);
     }
 
-  // Workspace layout: [MatDesc x nm][int tables] then per-matrix buffers.
+  // Workspace layout: [status header][MatDesc x nm][int tables] then
+  // per-matrix buffers. The header and the tables are uploaded together at
+  // the start of every call, which also clears the status word.
   P.desc_bytes = align_up(sizeof(MatDesc) * std::max(nm, 1));
-  P.table_bytes = P.desc_bytes + align_up(P.ints.size() * sizeof(int32_t));
+  P.table_bytes = kHeaderBytes + P.desc_bytes + align_up(P.ints.size() * sizeof(int32_t));
   size_t off = P.table_bytes;
   const size_t es = dtype_size(hp->ns_dtype);
   for (MatPlan& mp : P.mats) {
@@ -394,7 +413,7 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
     mp.off_x1 = off; off += xb;
     mp.off_a = off; off += ab;
     mp.off_b = off; off += ab;
-    mp.off_part = off; off += align_up(static_cast<size_t>(mp.ntile_ew) * 4);
+    mp.off_part = off; off += align_up(static_cast<size_t>(mp.ntile_ew) * sizeof(double));
     mp.off_stat = off; off += kAlign;
     mp.off_csr = off; off += align_up(static_cast<size_t>(mp.rp) * 4);
     mp.off_csc = off; off += align_up(static_cast<size_t>(mp.cp) * 4);
@@ -407,6 +426,93 @@ ma_status build_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* 
   }
   P.ws_bytes = off;
   return MA_OK;
+}
+
+// Plan cache. A training loop calls muon_step with the same tensor list every
+// step; its plan (expansion, buckets, tile maps, queues, layout) is built once
+// and kept, keyed by what structure_plan() reads. Validation still runs on
+// every call, and the descriptors (pointers, lr, wd) are filled per call.
+std::vector<int64_t> plan_key(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* hp) {
+  std::vector<int64_t> k;
+  k.reserve(4 + 4 * static_cast<size_t>(n) + 3 * static_cast<size_t>(hp->ns_steps));
+  k.push_back(n);
+  k.push_back(hp->ns_dtype);
+  k.push_back(hp->ns_steps);
+  for (int i = 0; i < n; ++i) {
+    if (!t[i].grad) {   // contributes no matrix
+      k.push_back(-1);
+      continue;
+    }
+    k.push_back(t[i].batch);
+    k.push_back(t[i].rows);
+    k.push_back(t[i].cols);
+    k.push_back(t[i].views);
+  }
+  for (int it = 0; it < hp->ns_steps; ++it)
+    for (int c = 0; c < 3; ++c) {
+      const float f = ns_coef(hp, it, c);
+      int32_t bits;
+      std::memcpy(&bits, &f, 4);
+      k.push_back(bits);
+    }
+  return k;
+}
+
+constexpr size_t kMaxCachedPlans = 64;
+std::mutex g_plan_mu;
+std::map<std::vector<int64_t>, std::shared_ptr<const Plan>> g_plans;
+
+// Validates the call and returns its plan, from the cache when the structure
+// has been seen before.
+ma_status get_plan(const ma_muon_tensor* t, int32_t n, const ma_muon_hparams* hp, bool ns_only,
+                   std::shared_ptr<const Plan>& out) {
+  ma_status st = validate_tensors(t, n, hp, ns_only);
+  if (st != MA_OK) return st;
+  std::vector<int64_t> key = plan_key(t, n, hp);
+  {
+    std::lock_guard<std::mutex> lk(g_plan_mu);
+    auto it = g_plans.find(key);
+    if (it != g_plans.end()) {
+      out = it->second;
+      return MA_OK;
+    }
+  }
+  auto P = std::make_shared<Plan>();
+  st = structure_plan(t, n, hp, *P);
+  if (st != MA_OK) return st;
+  std::lock_guard<std::mutex> lk(g_plan_mu);
+  if (g_plans.size() >= kMaxCachedPlans) g_plans.clear();
+  g_plans.emplace(std::move(key), P);
+  out = P;
+  return MA_OK;
+}
+
+// The persistent Newton-Schulz launch deals one task queue to each of 8 XCDs
+// and a block serves the queue of the XCD it runs on (XCC_ID), 32 blocks of
+// one CU each per XCD. It runs only on a device that reports 8 XCDs and at
+// least 256 CUs (an MI355X as one device); elsewhere, say on a partition of
+// the chip, the per-launch schedule runs instead. Cached per device.
+std::mutex g_topo_mu;
+std::map<int, bool> g_topo;
+
+bool device_runs_persistent() {
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess) return false;
+  std::lock_guard<std::mutex> lk(g_topo_mu);
+  auto it = g_topo.find(dev);
+  if (it != g_topo.end()) return it->second;
+  int cus = 0, xccs = 0;
+  bool ok = hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
+            cus >= kXcds * kPersistBlocksPerXcd;
+  if (ok && hipDeviceGetAttribute(&xccs, hipDeviceAttributeNumberOfXccs, dev) == hipSuccess) ok = xccs == kXcds;
+  (void)hipGetLastError();   // a runtime without the XCC attribute leaves no error behind
+  g_topo[dev] = ok;
+  return ok;
+}
+
+bool env_is(const char* name, const char* value) {
+  const char* v = std::getenv(name);
+  return v && std::string(v) == value;
 }
 
 TileMap device_map(const MapRef& r, char* tables, size_t desc_bytes) {
@@ -424,8 +530,10 @@ TileMap device_map(const MapRef& r, char* tables, size_t desc_bytes) {
   return tm;
 }
 
-// Pinned staging ring for the launch tables: a slot is reused only after the
-// copy it last fed has completed (an event from four calls earlier).
+// Pinned staging buffers for the launch tables. A buffer is reused once the
+// copy it last fed has completed (its event has fired); while none has, a new
+// one joins the pool, up to kMaxStaging per device, so the host waits for the
+// device only when it runs that many calls ahead of it.
 struct Staging {
   void* host = nullptr;
   size_t cap = 0;
@@ -433,9 +541,10 @@ struct Staging {
   bool used = false;
 };
 struct DevState {
-  Staging ring[4];
-  unsigned next = 0;
+  std::vector<Staging> pool;
+  size_t next = 0;
 };
+constexpr size_t kMaxStaging = 64;
 std::mutex g_mu;
 std::map<int, DevState> g_dev;
 
@@ -444,8 +553,28 @@ ma_status upload(const std::vector<char>& host, void* dst, hipStream_t s) {
   if (hipGetDevice(&dev) != hipSuccess) return fail(MA_E_HIP, "hipGetDevice failed");
   std::lock_guard<std::mutex> lk(g_mu);
   DevState& ds = g_dev[dev];
-  Staging& st = ds.ring[ds.next++ % 4];
-  if (st.used && hipEventSynchronize(st.ev) != hipSuccess) return fail(MA_E_HIP, "staging event wait failed");
+  size_t pick = ds.pool.size();
+  for (size_t k = 0; k < ds.pool.size() && pick == ds.pool.size(); ++k) {
+    const size_t i = (ds.next + k) % ds.pool.size();
+    Staging& c = ds.pool[i];
+    if (!c.used) {
+      pick = i;
+      break;
+    }
+    const hipError_t q = hipEventQuery(c.ev);
+    if (q == hipSuccess) pick = i;
+    else if (q != hipErrorNotReady) return fail(MA_E_HIP, "staging event query failed");
+  }
+  if (pick == ds.pool.size()) {
+    if (ds.pool.size() < kMaxStaging) {
+      ds.pool.emplace_back();
+    } else {   // every buffer still in flight: wait for the oldest
+      pick = ds.next % ds.pool.size();
+      if (hipEventSynchronize(ds.pool[pick].ev) != hipSuccess) return fail(MA_E_HIP, "staging event wait failed");
+    }
+  }
+  ds.next = pick + 1;
+  Staging& st = ds.pool[pick];
   if (st.cap < host.size()) {
     if (st.host) (void)hipHostFree(st.host);
     st.host = nullptr;
@@ -509,8 +638,12 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
   const int nm = static_cast<int>(P.mats.size());
   if (nm == 0) return MA_OK;
   char* base = static_cast<char*>(ws);
-  std::vector<char> host(P.table_bytes, 0);
-  MatDesc* D = reinterpret_cast<MatDesc*>(host.data());
+  char* tables = base + kHeaderBytes;   // descriptors, then the int tables
+  // operand layout of SQUARE and APPLY: by size unless the environment
+  // forces one (the results are the same bits either way)
+  const int operands = env_is("MA_NS_OPERANDS", "kmajor") ? 1 : (env_is("MA_NS_OPERANDS", "rows") ? 2 : 0);
+  std::vector<char> host(P.table_bytes, 0);   // the header (status word 0) and the tables
+  MatDesc* D = reinterpret_cast<MatDesc*>(host.data() + kHeaderBytes);
   for (int k = 0; k < nm; ++k) {
     const MatPlan& mp = P.mats[k];
     const ma_muon_tensor& x = t[mp.tensor];
@@ -536,7 +669,7 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
     d.x1 = base + mp.off_x1;
     d.a = base + mp.off_a;
     d.b = base + mp.off_b;
-    d.part = reinterpret_cast<float*>(base + mp.off_part);
+    d.part = reinterpret_cast<double*>(base + mp.off_part);
     d.stat = reinterpret_cast<float*>(base + mp.off_stat);
     d.csum_r = reinterpret_cast<float*>(base + mp.off_csr);
     d.csum_c = reinterpret_cast<float*>(base + mp.off_csc);
@@ -544,39 +677,44 @@ ma_status run_plan(const Plan& P, const ma_muon_tensor* t, const ma_muon_hparams
     d.cfac = reinterpret_cast<float*>(base + mp.off_cf);
     d.ntile_ew = mp.ntile_ew;
     d.clip = ns_only ? nullptr : hp->clip;
-    d.kmajor = P.operands == 1 || (P.operands == 0 && mp.rp <= kKmajorMaxRows);
+    d.kmajor = operands == 1 || (operands == 0 && mp.rp <= kKmajorMaxRows);
   }
-  std::memcpy(host.data() + P.desc_bytes, P.ints.data(), P.ints.size() * sizeof(int32_t));
+  std::memcpy(host.data() + kHeaderBytes + P.desc_bytes, P.ints.data(), P.ints.size() * sizeof(int32_t));
   ma_status st = upload(host, ws, s);
   if (st != MA_OK) return st;
 
-  const MatDesc* mats = reinterpret_cast<const MatDesc*>(base);
-  auto TM = [&](const MapRef& r) { return device_map(r, base, P.desc_bytes); };
+  const MatDesc* mats = reinterpret_cast<const MatDesc*>(tables);
+  auto TM = [&](const MapRef& r) { return device_map(r, tables, P.desc_bytes); };
   const float beta = static_cast<float>(hp->beta);
   const float omb = static_cast<float>(1.0 - hp->beta);
   (void)hipGetLastError();
   const int ew_dt = P.ns_dt;
   timed("momentum", s, [&] { launch_momentum(mats, TM(P.ew), ew_dt, beta, omb, hp->nesterov, s); });
   timed("norm_finalize", s,
-        [&] { launch_norm_finalize(mats, TM(P.fin_all), hp->ns_eps, ns_norm_scale(hp), s); });
+        [&] { launch_norm_finalize(mats, TM(P.fin_all), P.ns_dt, hp->ns_eps, ns_norm_scale(hp), s); });
   static const char* const kNsNames[2][3] = {{"ns_gram_f32", "ns_square_f32", "ns_apply_f32"},
                                              {"ns_gram_bf16", "ns_square_bf16", "ns_apply_bf16"}};
   const int bf = P.ns_dt == MA_BF16;
-  if (P.persist) {
+  // the persistent schedule unless the device cannot run it or the
+  // environment asks for one launch per product (MA_NS_SCHEDULE=launches)
+  const bool persist = P.persist && !env_is("MA_NS_SCHEDULE", "launches") && device_runs_persistent();
+  if (persist) {
     NsQueue q;
-    q.segs = reinterpret_cast<const int4*>(base + P.desc_bytes + P.segs_off);
+    q.segs = reinterpret_cast<const int4*>(tables + P.desc_bytes + P.segs_off);
     q.qhead = reinterpret_cast<int*>(base + P.off_counters);
     q.err = q.qhead + 8 * 32;
     q.count = q.err + 32;
+    q.status = reinterpret_cast<int*>(base);
     for (int x = 0; x < 8; ++x) {
       q.seg_off[x] = P.seg_off[x];
       q.nseg[x] = P.nseg[x];
     }
-    q.coefs = reinterpret_cast<const float*>(base + P.desc_bytes + P.coefs_off);
+    q.coefs = reinterpret_cast<const float*>(tables + P.desc_bytes + P.coefs_off);
     q.clip = ns_only ? nullptr : hp->clip;
     timed("ns_persistent_bf16", s, [&] { launch_ns_persistent(mats, q, P.counter_ints, s); });
+    timed("ns_status", s, [&] { launch_ns_status(q, s); });
   }
-  for (int it = 0; it < (P.persist ? 0 : hp->ns_steps); ++it) {
+  for (int it = 0; it < (persist ? 0 : hp->ns_steps); ++it) {
     for (int op = NS_GRAM; op <= NS_APPLY; ++op) {
       const TileMap tm = TM(op == NS_APPLY ? P.app : (op == NS_GRAM ? P.gram : P.sq));
       timed(kNsNames[bf][op], s, [&] {
@@ -654,19 +792,19 @@ extern "C" {
 const char* ma_last_error(void) { return g_err.c_str(); }
 
 size_t ma_muon_workspace_bytes(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp) {
-  Plan P;
-  if (build_plan(tensors, n, hp, false, P) != MA_OK) return 0;
-  return P.mats.empty() ? 0 : P.ws_bytes;
+  std::shared_ptr<const Plan> P;
+  if (get_plan(tensors, n, hp, false, P) != MA_OK) return 0;
+  return P->mats.empty() ? 0 : P->ws_bytes;
 }
 
 ma_status muon_step(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp, void* workspace,
                     size_t workspace_bytes, void* stream) {
-  Plan P;
-  ma_status st = build_plan(tensors, n, hp, false, P);
+  std::shared_ptr<const Plan> P;
+  ma_status st = get_plan(tensors, n, hp, false, P);
   if (st != MA_OK) return st;
-  st = check_workspace(P, workspace, workspace_bytes);
+  st = check_workspace(*P, workspace, workspace_bytes);
   if (st != MA_OK) return st;
-  return run_plan(P, tensors, hp, false, workspace, static_cast<hipStream_t>(stream));
+  return run_plan(*P, tensors, hp, false, workspace, static_cast<hipStream_t>(stream));
 }
 
 size_t ma_newton_schulz_workspace_bytes(int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
@@ -678,9 +816,9 @@ size_t ma_newton_schulz_workspace_bytes(int64_t batch, int64_t rows, int64_t col
   alignas(16) static const char dummy[16] = {0};
   ma_muon_tensor x = ns_tensor(dummy, const_cast<char*>(dummy), batch, rows, cols, dtype);
   ma_muon_hparams h = ns_hparams(hp);
-  Plan P;
-  if (build_plan(&x, 1, &h, true, P) != MA_OK) return 0;
-  return P.ws_bytes;
+  std::shared_ptr<const Plan> P;
+  if (get_plan(&x, 1, &h, true, P) != MA_OK) return 0;
+  return P->ws_bytes;
 }
 
 ma_status ma_newton_schulz(const void* in, void* out, int64_t batch, int64_t rows, int64_t cols, int32_t dtype,
@@ -689,32 +827,44 @@ ma_status ma_newton_schulz(const void* in, void* out, int64_t batch, int64_t row
   if (!in || !out) return fail(MA_E_INVALID, "in/out is NULL");
   ma_muon_tensor x = ns_tensor(in, out, batch, rows, cols, dtype);
   ma_muon_hparams h = ns_hparams(hp);
-  Plan P;
-  ma_status st = build_plan(&x, 1, &h, true, P);
+  std::shared_ptr<const Plan> P;
+  ma_status st = get_plan(&x, 1, &h, true, P);
   if (st != MA_OK) return st;
-  st = check_workspace(P, workspace, workspace_bytes);
+  st = check_workspace(*P, workspace, workspace_bytes);
   if (st != MA_OK) return st;
-  return run_plan(P, &x, &h, true, workspace, static_cast<hipStream_t>(stream));
+  return run_plan(*P, &x, &h, true, workspace, static_cast<hipStream_t>(stream));
+}
+
+ma_status ma_muon_step_status(const void* workspace, int32_t* status, void* stream) {
+  if (!workspace || !status) return fail(MA_E_INVALID, "workspace and status must not be NULL");
+  if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(MA_E_WORKSPACE, "workspace must be 256-byte aligned");
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  int32_t v = 0;
+  if (hipMemcpyAsync(&v, workspace, sizeof(v), hipMemcpyDeviceToHost, s) != hipSuccess)
+    return fail(MA_E_HIP, "status read failed");
+  if (hipStreamSynchronize(s) != hipSuccess) return fail(MA_E_HIP, "stream synchronisation failed");
+  *status = v;
+  return MA_OK;
 }
 
 ma_status ma_muon_plan_counts(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
                               int32_t* n_matrices, int32_t* n_buckets) {
-  Plan P;
-  ma_status st = build_plan(tensors, n, hp, false, P);
+  std::shared_ptr<const Plan> P;
+  ma_status st = get_plan(tensors, n, hp, false, P);
   if (st != MA_OK) return st;
-  if (n_matrices) *n_matrices = static_cast<int32_t>(P.mats.size());
-  if (n_buckets) *n_buckets = P.nbuckets;
+  if (n_matrices) *n_matrices = static_cast<int32_t>(P->mats.size());
+  if (n_buckets) *n_buckets = P->nbuckets;
   return MA_OK;
 }
 
 ma_status ma_muon_matrix_info(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp, int32_t k,
                               ma_matrix_info* info) {
   if (!info) return fail(MA_E_INVALID, "info is NULL");
-  Plan P;
-  ma_status st = build_plan(tensors, n, hp, false, P);
+  std::shared_ptr<const Plan> P;
+  ma_status st = get_plan(tensors, n, hp, false, P);
   if (st != MA_OK) return st;
-  if (k < 0 || k >= static_cast<int32_t>(P.mats.size())) return fail(MA_E_INVALID, "matrix index out of range");
-  const MatPlan& mp = P.mats[k];
+  if (k < 0 || k >= static_cast<int32_t>(P->mats.size())) return fail(MA_E_INVALID, "matrix index out of range");
+  const MatPlan& mp = P->mats[k];
   std::memset(info, 0, sizeof(*info));
   info->tensor = mp.tensor;
   info->batch_index = mp.bidx;
@@ -810,7 +960,7 @@ ma_status validate_grads(const ma_grad_ref* grads, int32_t n, int64_t& blocks) {
 size_t ma_grad_norm_workspace_bytes(const ma_grad_ref* grads, int32_t n) {
   int64_t blocks = 0;
   if (validate_grads(grads, n, blocks) != MA_OK) return 0;
-  return align_up(static_cast<size_t>(std::max<int64_t>(blocks, 1)) * sizeof(float));
+  return align_up(static_cast<size_t>(std::max<int64_t>(blocks, 1)) * sizeof(double));
 }
 
 ma_status ma_global_grad_norm(const ma_grad_ref* grads, int32_t n, float max_norm, float* state, void* workspace,
@@ -820,14 +970,14 @@ ma_status ma_global_grad_norm(const ma_grad_ref* grads, int32_t n, float max_nor
   if (st != MA_OK) return st;
   if (!std::isfinite(max_norm)) return fail(MA_E_INVALID, "max_norm must be finite");
   if (!state || reinterpret_cast<uintptr_t>(state) % 16) return fail(MA_E_INVALID, "state must be a 16-byte aligned device pointer");
-  const size_t need = align_up(static_cast<size_t>(std::max<int64_t>(blocks, 1)) * sizeof(float));
+  const size_t need = align_up(static_cast<size_t>(std::max<int64_t>(blocks, 1)) * sizeof(double));
   if (!workspace) return fail(MA_E_WORKSPACE, "workspace is NULL");
   if (reinterpret_cast<uintptr_t>(workspace) % kAlign) return fail(MA_E_WORKSPACE, "workspace must be 256-byte aligned");
   if (workspace_bytes < need)
     return fail(MA_E_WORKSPACE, "workspace too small: " + std::to_string(workspace_bytes) + " < " + std::to_string(need));
   hipStream_t s = static_cast<hipStream_t>(stream);
   (void)hipGetLastError();
-  float* partial = static_cast<float*>(workspace);
+  double* partial = static_cast<double*>(workspace);
   GradNormLaunch L{};
   L.partial = partial;
   int64_t done_blocks = 0, blocks_here = 0;

@@ -44,8 +44,9 @@ struct MatDesc {
   void* x1;           // canonical rp x cp, ns dtype: X1, X3, X5
   void* a;            // rp x rp Gram
   void* b;            // rp x rp  b*A + c*A^2
-  float* part;        // sum-of-squares partial per momentum-pass tile
-  float* stat;        // [0] sigma = 1/(||Q||_F + eps)
+  double* part;       // sum-of-squares partial per momentum-pass tile (fp64: no overflow)
+  float* stat;        // [0] sigma = 1/(||Q||_F + eps) of X0; [1] the power of two X0 was
+                      // scaled by against an overflow of the first Gram (1: not scaled)
   float* csum_r;      // canonical row sums of squares, rp entries
   float* csum_c;      // canonical column sums of squares, cp entries
   float* rfac;        // per stored row factor, m entries
@@ -89,6 +90,7 @@ struct NsQueue {
   int* qhead;
   int* err;
   int* count;
+  int* status;          // the step's status word (first int of the workspace)
   const float* coefs;   // (a, b, c) of each iteration, 3 floats per iteration
   const float* clip;    // the step's clip state or null: a skipped step runs no tile
   int32_t seg_off[8];
@@ -148,6 +150,12 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, int dt, float v) 
 
 // Wave64 sum in a fixed butterfly order (deterministic).
 __device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
+  return v;
+}
+
+__device__ __forceinline__ double wave_sum(double v) {
 #pragma unroll
   for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, 64);
   return v;

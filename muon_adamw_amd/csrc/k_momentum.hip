@@ -8,7 +8,7 @@
 // element with a bf16 Q). One 64x64 canonical tile per block; a tall matrix is
 // transposed through LDS. The reduction always walks the canonical tile in the
 // same thread order, so a tall matrix and its transposed wide twin produce the
-// same bits.
+// same bits. Squares and partials are fp64, so no finite Q overflows them.
 #include "kernels.hpp"
 
 namespace ma {
@@ -30,12 +30,12 @@ __device__ __forceinline__ void store4<uint16_t>(uint16_t* dst, const float* v) 
   *gmem(reinterpret_cast<gu2*>(dst)) = p;
 }
 
-__device__ __forceinline__ float block_sum_256(float v, float* red) {
+__device__ __forceinline__ double block_sum_256(double v, double* red) {
   v = wave_sum(v);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   if (lane == 0) red[w] = v;
   __syncthreads();
-  float t = ((red[0] + red[1]) + red[2]) + red[3];
+  double t = ((red[0] + red[1]) + red[2]) + red[3];
   __syncthreads();
   return t;
 }
@@ -44,7 +44,7 @@ template <typename XT>
 __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict__ mats, TileMap tm,
                                                        float beta, float omb, int nesterov) {
   __shared__ float qs[kEw][kEw + 1];
-  __shared__ float red[4];
+  __shared__ double red[4];
   const int blk = blockIdx.x;
   const int e = find_entry(tm, blk);
   const MatDesc& d = mats[tm.perm[e]];
@@ -127,9 +127,11 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
   }
   __syncthreads();
 
-  // Phase 2: canonical tile, same thread order for both orientations.
+  // Phase 2: canonical tile, same thread order for both orientations. The
+  // squares are summed in fp64: an fp32 square overflows above |Q| ~ 1.8e19,
+  // where the norm itself is still finite.
   XT* X = static_cast<XT*>(d.x0);
-  float ss = 0.f;
+  double ss = 0.0;
 #pragma unroll
   for (int p = 0; p < 4; ++p) {
     const int ci = tr + 16 * p;
@@ -137,22 +139,49 @@ __global__ __launch_bounds__(256) void momentum_kernel(const MatDesc* __restrict
 #pragma unroll
     for (int u = 0; u < 4; ++u) {
       v[u] = d.tall ? qs[tc + u][ci] : qs[ci][tc + u];
-      ss += v[u] * v[u];
+      ss += static_cast<double>(v[u]) * static_cast<double>(v[u]);
     }
     store4<XT>(X + (int64_t)(i0 + ci) * d.cp + j0 + tc, v);
   }
-  const float tot = block_sum_256(ss, red);
+  const double tot = block_sum_256(ss, red);
   if (threadIdx.x == 0) gmem(d.part)[t] = tot;
 }
 
+// Above this Frobenius norm of Q the first Gram's fp32 sums, which are
+// bounded by ||Q||_F^2 and computed before sigma^2 is applied, could reach the
+// fp32 range (2^128); such an X0 is scaled down to a norm near 2^kGuardTarget.
+constexpr int kGuardExp = 60;
+constexpr int kGuardTarget = 30;
+
+template <typename XT>
 __global__ __launch_bounds__(256) void norm_finalize_kernel(const MatDesc* __restrict__ mats, TileMap tm,
                                                             float eps, float scale) {
-  __shared__ float red[4];
+  __shared__ double red[4];
   const MatDesc& d = mats[tm.perm[blockIdx.x]];
-  float s = 0.f;
+  double s = 0.0;
   for (int i = threadIdx.x; i < d.ntile_ew; i += 256) s += gmem(d.part)[i];
-  const float tot = block_sum_256(s, red);
-  if (threadIdx.x == 0) gmem(d.stat)[0] = 1.0f / (sqrtf(tot) * scale + eps);
+  const double tot = block_sum_256(s, red);
+  const double norm = sqrt(tot);
+  // X = Q / (norm * scale + eps) = (2^-k Q) * 2^k / (norm * scale + eps):
+  // with k > 0 the stored X0 is scaled by the power of two 2^-k (exact) and
+  // sigma carries 2^k
+  int k = 0;
+  if (isfinite(norm) && norm >= ldexp(1.0, kGuardExp)) k = ilogb(norm) - kGuardTarget;
+  const double sigma = 1.0 / (norm * static_cast<double>(scale) + static_cast<double>(eps));
+  if (threadIdx.x == 0) {
+    gmem(d.stat)[0] = static_cast<float>(ldexp(sigma, k));
+    gmem(d.stat)[1] = ldexpf(1.0f, -k);
+  }
+  if (k == 0 || step_skipped(d.clip)) return;
+  const float f = ldexpf(1.0f, -k);
+  XT* X = static_cast<XT*>(d.x0);
+  const int64_t n = static_cast<int64_t>(d.rp) * d.cp;
+  for (int64_t i = threadIdx.x; i < n; i += 256) {
+    if constexpr (sizeof(XT) == 2)
+      gmem(X)[i] = f32_to_bf16(bf16_to_f32(gmem(X)[i]) * f);
+    else
+      gmem(X)[i] = gmem(X)[i] * f;
+  }
 }
 
 }  // namespace
@@ -166,9 +195,12 @@ void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, flo
     hipLaunchKernelGGL(momentum_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, beta, omb, nesterov);
 }
 
-void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, float scale, hipStream_t s) {
+void launch_norm_finalize(const MatDesc* mats, TileMap tm, int ns_dt, float eps, float scale, hipStream_t s) {
   if (tm.total == 0) return;
-  hipLaunchKernelGGL(norm_finalize_kernel, dim3(tm.grid), dim3(256), 0, s, mats, tm, eps, scale);
+  if (ns_dt == DT_BF16)
+    hipLaunchKernelGGL(norm_finalize_kernel<uint16_t>, dim3(tm.grid), dim3(256), 0, s, mats, tm, eps, scale);
+  else
+    hipLaunchKernelGGL(norm_finalize_kernel<float>, dim3(tm.grid), dim3(256), 0, s, mats, tm, eps, scale);
 }
 
 }  // namespace ma

@@ -662,6 +662,25 @@ __global__ __launch_bounds__(NTHR, 1) void ns_persistent_kernel(const MatDesc* _
   }
 }
 
+// The outcome of the persistent launch, in the step's status word: bit 0 a
+// bounded wait ran out (a tile may then have read operands before they were
+// complete), bit 1 an XCD's queue was not handed out to its end (no block
+// ran on that XCD, so its matrices were left unfinished). A skipped step ran
+// no tile and reports 0. One thread; runs after the launch on its stream, so
+// the counters it reads are final.
+__global__ void ns_status_kernel(NsQueue q) {
+  if (threadIdx.x != 0) return;
+  int st = 0;
+  if (!step_skipped(q.clip)) {
+    if (gmem(q.err)[0] != 0) st |= NS_STATUS_WAIT_TIMEOUT;
+    for (int x = 0; x < 8; ++x) {
+      const int total = q.nseg[x] ? q.segs[q.seg_off[x] + q.nseg[x]].z : 0;
+      if (gmem(q.qhead)[32 * x] < total) st |= NS_STATUS_QUEUE_UNDRAINED;
+    }
+  }
+  gmem(q.status)[0] = st;
+}
+
 __global__ void zero_ints_kernel(int* p, int n) {
   for (int i = blockIdx.x * blockDim.x + threadIdx.x; i < n; i += gridDim.x * blockDim.x) gmem(p)[i] = 0;
 }
@@ -671,6 +690,10 @@ __global__ void zero_ints_kernel(int* p, int n) {
 void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, hipStream_t s) {
   hipLaunchKernelGGL(zero_ints_kernel, dim3(16), dim3(256), 0, s, q.qhead, zero_ints);
   hipLaunchKernelGGL(ns_persistent_kernel, dim3(8 * kPersistBlocksPerXcd), dim3(NTHR), 0, s, mats, q);
+}
+
+void launch_ns_status(const NsQueue& q, hipStream_t s) {
+  hipLaunchKernelGGL(ns_status_kernel, dim3(1), dim3(64), 0, s, q);
 }
 
 void launch_ns_bf16(int op, const MatDesc* mats, TileMap tm, int src, int first, float a, float b, float c,

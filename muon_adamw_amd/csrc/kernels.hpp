@@ -9,8 +9,10 @@ namespace ma {
 // Frobenius partials (speedtronic "Muon update", first two lines).
 void launch_momentum(const MatDesc* mats, TileMap tm, int ns_dt, float beta, float one_minus_beta,
                      int nesterov, hipStream_t s);
-// sigma = 1 / (sqrt(sum of partials) * scale + eps), one block per matrix, fixed order.
-void launch_norm_finalize(const MatDesc* mats, TileMap tm, float eps, float scale, hipStream_t s);
+// sigma = 1 / (sqrt(sum of partials) * scale + eps), one block per matrix, fixed
+// order in fp64. A matrix whose norm could overflow the fp32 sums of the first
+// Gram has its X0 scaled by a power of two there, and sigma compensates.
+void launch_norm_finalize(const MatDesc* mats, TileMap tm, int ns_dt, float eps, float scale, hipStream_t s);
 
 // One product of a Newton-Schulz iteration over every matrix (op 0: Gram
 // A = s2 * X X^T, lower-triangle tiles mirrored; op 1: B = b A + c A A^T, A
@@ -26,6 +28,10 @@ void launch_ns_f32(int op, const MatDesc* mats, TileMap tm, int src, int first, 
 // error word and the completion counters).
 // The coefficients of iteration it are q.coefs[3 it .. 3 it + 2].
 void launch_ns_persistent(const MatDesc* mats, const NsQueue& q, int zero_ints, hipStream_t s);
+// After the persistent launch: writes q.status (bit 0: a bounded wait ran out,
+// bit 1: a queue was not handed out to its end; 0 on a skipped step).
+enum : int { NS_STATUS_WAIT_TIMEOUT = 1, NS_STATUS_QUEUE_UNDRAINED = 2 };
+void launch_ns_status(const NsQueue& q, hipStream_t s);
 
 // Sums of squares of the final Newton-Schulz output along canonical rows
 // (csum_r) or canonical columns (csum_c), optionally weighted by the square
@@ -79,8 +85,9 @@ __host__ __device__ inline uint64_t splitmix64_mix(uint64_t z) {
 }
 void launch_adamw(const AdamLaunch& L, int nblocks, hipStream_t s);
 
-// Global gradient norm: per-chunk fp32 partial sums of g^2, then one block
-// that adds them in fp64 in a fixed order and writes the clip state.
+// Global gradient norm: per-chunk fp64 partial sums of g^2 (an fp32 square
+// overflows above |g| ~ 1.8e19), then one block that adds them in fp64 in a
+// fixed order and writes the clip state.
 struct GradNormArg {
   const void* g;
   int64_t numel;
@@ -93,10 +100,10 @@ struct GradNormLaunch {
   GradNormArg t[kMaxGradNormTensors];
   int32_t block_start[kMaxGradNormTensors + 1];
   int32_t nt;
-  float* partial;      // one fp32 per block of all launches
+  double* partial;     // one fp64 per block of all launches
   int32_t partial_off; // this launch's first partial
 };
 void launch_grad_sumsq(const GradNormLaunch& L, int nblocks, hipStream_t s);
-void launch_grad_norm_finalize(const float* partial, int n, float max_norm, float* state, hipStream_t s);
+void launch_grad_norm_finalize(const double* partial, int n, float max_norm, float* state, hipStream_t s);
 
 }  // namespace ma

@@ -445,3 +445,90 @@ def test_matrix_expansion_matches_the_oracle_on_random_lists(lib):
             assert mi.scale == pytest.approx(omuon.shape_scale(m, cols), rel=1e-7)
             assert mi.bucket == buckets.setdefault((rr, cc), len(buckets))
         assert nb == len(buckets)
+
+
+def test_plan_cache_still_validates_every_call(lib):
+    """A cached plan skips the planning, never the validation: the same
+    structure with a misaligned or an aliased pointer is still rejected."""
+    wl = workloads.workload(2)
+    n = len(wl.muon)
+    hp = hp_of(wl)
+    arr = fake_descs(wl)
+    assert lib.ma_muon_workspace_bytes(arr, n, ctypes.byref(hp)) > 0   # plan now cached
+    bad = fake_descs(wl)
+    bad[3].param = bad[3].param + 2                    # fp32 parameter off its 4-byte alignment
+    assert step(lib, bad, n, hp) == 1 and b"aligned" in lib.ma_last_error()
+    alias = fake_descs(wl)
+    alias[5].momentum = alias[4].momentum              # two tensors sharing momentum
+    assert step(lib, alias, n, hp) == 3
+    nan_lr = fake_descs(wl)
+    nan_lr[0].lr = float("nan")
+    assert step(lib, nan_lr, n, hp) == 1
+
+
+def test_plan_does_not_depend_on_pointers_or_values(lib):
+    """Two lists of the same structure at other addresses, with other lr and
+    wd, get the same workspace size and the same matrix layout."""
+    wl = workloads.workload(4)
+    n = len(wl.muon)
+    hp = hp_of(wl)
+    a = fake_descs(wl)
+    b = fake_descs(wl, gap=1 << 36)
+    for i in range(n):
+        b[i].lr, b[i].weight_decay = 0.5, 0.0
+    assert lib.ma_muon_workspace_bytes(a, n, ctypes.byref(hp)) == lib.ma_muon_workspace_bytes(b, n, ctypes.byref(hp))
+    for k in (0, 63, 64, 191):
+        x, y = info(lib, a, n, hp, k), info(lib, b, n, hp, k)
+        assert bytes(x) == bytes(y), k
+
+
+def test_plan_follows_structure_changes(lib):
+    """Whatever the plan depends on is in its key: a tensor losing its
+    gradient, a changed view count or shape, a changed step count."""
+    wl = workloads.workload(2)
+    n = len(wl.muon)
+    hp = hp_of(wl)
+    arr = fake_descs(wl)
+    assert counts(lib, arr, n, hp)[1] == 72
+    arr[0].grad = None
+    assert counts(lib, arr, n, hp)[1] == 71
+    arr = fake_descs(wl)
+    arr[4].views = 2                                   # 3072x768 up as two 1536x768 views
+    assert counts(lib, arr, n, hp)[1:] == (73, 3)
+    assert (info(lib, arr, n, hp, 4).m, info(lib, arr, n, hp, 5).view) == (1536, 1)
+    arr = fake_descs(wl)
+    arr[0].rows = 384
+    assert info(lib, arr, n, hp, 0).m == 384
+    arr = fake_descs(wl)
+    hp3 = hp_of(wl)
+    hp3.ns_steps = 3                                   # the final output moves to the other buffer
+    i5, i3 = info(lib, arr, n, hp, 0), info(lib, arr, n, hp3, 0)
+    assert i5.u_offset != i3.u_offset
+
+
+def test_workspace_starts_with_the_status_header(lib):
+    """The first 256 bytes of a Muon workspace are the status header; the
+    descriptors and tables follow, then the matrix buffers."""
+    wl = workloads.workload(2)
+    n = len(wl.muon)
+    hp = hp_of(wl)
+    arr = fake_descs(wl)
+    first = min(min(info(lib, arr, n, hp, k).u_offset, info(lib, arr, n, hp, k).a_offset) for k in range(72))
+    assert first >= 256 + 72 * 176
+    assert first % 256 == 0
+
+
+def test_step_status_query_validation(lib):
+    st = ctypes.c_int32(-1)
+    assert lib.ma_muon_step_status(None, ctypes.byref(st), None) == 1
+    assert lib.ma_muon_step_status(BASE, None, None) == 1
+    assert lib.ma_muon_step_status(BASE + 16, ctypes.byref(st), None) == 4
+    assert st.value == -1
+
+
+def test_grad_norm_partials_are_fp64(lib):
+    """One fp64 partial per 8192-element chunk, rounded up to 256 bytes."""
+    g = (ma.GradRefC * 2)()
+    g[0].grad, g[0].numel, g[0].dtype = BASE, 8192 * 100, ma.MA_F32
+    g[1].grad, g[1].numel, g[1].dtype = BASE + (1 << 30), 8192 * 27 + 1, ma.MA_BF16
+    assert lib.ma_grad_norm_workspace_bytes(g, 2) == 1024     # 128 partials x 8 bytes

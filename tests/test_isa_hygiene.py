@@ -86,3 +86,81 @@ def test_newton_schulz_kernels_do_not_spill(asm):
         assert priv == 0, name
         assert "scratch_" not in body, name
     assert found > 0
+
+
+# The direct loads read M0 (the LDS destination) as well as their VGPR
+# address. The hazard rules of the GCN/CDNA ISA for that operand: an SALU
+# write of M0 needs one wait state before a load that writes LDS through it,
+# and a VALU write of an SGPR (v_readfirstlane and friends) needs five before
+# a VMEM instruction reads it. The check walks back from every direct load
+# over the instructions in front of it.
+_INSTR = re.compile(r"^\s+([a-z_][a-z0-9_]*)\b(.*)$")
+
+
+def _instructions(text):
+    """(opcode, operands) per instruction; a branch target label becomes
+    ("<label>", name), since control can enter there from elsewhere."""
+    out = []
+    for line in text.splitlines():
+        if re.match(r"^\.?L\w*:", line):
+            out.append(("<label>", line.split(":")[0]))
+            continue
+        m = _INSTR.match(line)
+        if m and not line.lstrip().startswith((";", ".")):
+            out.append((m.group(1), m.group(2).split(";")[0].strip()))
+    return out
+
+
+def _writes_m0(op, args):
+    return args.split(",")[0].strip() == "m0" and not op.startswith(("global_", "buffer_", "ds_", "s_waitcnt"))
+
+
+def _wait_states(op, args):
+    if op == "s_nop":
+        return int(args, 0) + 1
+    return 1
+
+
+def m0_hazards(text):
+    """(index, reason) for every direct load whose M0 write comes too close."""
+    ins = _instructions(text)
+    bad = []
+    for i, (op, args) in enumerate(ins):
+        if not op.startswith("global_load_lds_dword"):
+            continue
+        states, found = 0, False
+        for j in range(i - 1, max(-1, i - 64), -1):
+            pop, pargs = ins[j]
+            if _writes_m0(pop, pargs):
+                need = 1 if pop.startswith("s_") else 5
+                if states < need:
+                    bad.append((i, f"{pop} {pargs} then {states} wait state(s) before {op}"))
+                found = True
+                break
+            if pop == "<label>" or pop.startswith(("s_branch", "s_cbranch", "s_setpc", "s_endpgm")):
+                break
+            states += _wait_states(pop, pargs)
+        if not found:   # M0 set in another basic block: not provable from here
+            bad.append((i, f"no M0 write in the straight-line code before {op}"))
+    return bad
+
+
+def test_m0_hazard_check_catches_close_writes():
+    ok = "\ts_mov_b32 m0, s4\n\ts_nop 0\n\tglobal_load_lds_dwordx4 v[0:1], off\n"
+    assert m0_hazards(ok) == []
+    salu_close = "\ts_mov_b32 m0, s4\n\tglobal_load_lds_dwordx4 v[0:1], off\n"
+    assert len(m0_hazards(salu_close)) == 1
+    valu = "\tv_readfirstlane_b32 m0, v4\n\ts_nop 0\n\tv_add_u32 v1, v2, v3\n\tglobal_load_lds_dwordx4 v[0:1], off\n"
+    assert len(m0_hazards(valu)) == 1
+    valu_far = "\tv_readfirstlane_b32 m0, v4\n\ts_nop 4\n\tglobal_load_lds_dwordx4 v[0:1], off\n"
+    assert m0_hazards(valu_far) == []
+    across_label = "\ts_mov_b32 m0, s4\n\ts_nop 0\n.LBB0_3:\n\tglobal_load_lds_dwordx4 v[0:1], off\n"
+    assert len(m0_hazards(across_label)) == 1
+
+
+def test_direct_loads_respect_m0_wait_states(asm):
+    n = 0
+    for src, text in asm.items():
+        n += text.count("global_load_lds_dword")
+        assert m0_hazards(text) == [], src
+    assert n > 0
