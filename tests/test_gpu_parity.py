@@ -218,6 +218,7 @@ def run_and_check_muon(k, matrix_filter=None, oracle_filter=None, tol_ns=2e-2):
                    snapshot(data.muon[ti].row_v)) for ti in tens}
     flush(f"workload {wl.name}: muon_step ({len(sel)} of {nmat} matrices checked)")
     ws = ma.muon_step(params, hp)
+    assert ma.muon_step_status(ws) == 0
     torch.cuda.synchronize()
     for kk in sel:
         info = infos[kk]
