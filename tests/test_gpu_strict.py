@@ -291,7 +291,8 @@ def test_huge_gradients_clip_instead_of_skipping():
     inp = oracle_inputs(data)
     n = 70000
     p, g = randn((n,), 90, 0.02), randn((n,), 91, 1e20)
-    ap = [ma.AdamWParam(p.to(DEV), g.to(DEV), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV), 1e-3, 0.1)]
+    ap = [ma.AdamWParam(p.clone().to(DEV), g.clone().to(DEV), torch.zeros(n, device=DEV), torch.zeros(n, device=DEV),
+                        1e-3, 0.1)]
     grads = [t.grad for t in data.muon] + [ap[0].grad]
     want_norm = ognorm.global_norm([(workloads.to_numpy(x), "f32") for x in grads])
     assert math.isfinite(want_norm) and want_norm > 1e21
