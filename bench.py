@@ -115,6 +115,45 @@ def elementwise_bytes(wl):
     return {"momentum": mom, "apply_update": app, "adamw": adam}
 
 
+def reduction_bytes(wl):
+    """Algorithmic HBM bytes per step of the NorMuon / Muon+ reductions: one
+    read of U (ns dtype) per pass. A canonical-row pass covers the wide
+    matrices (NorMuon; Muon+ stage 1) and, with Muon+, the tall ones in stage 2;
+    a canonical-column pass the other way round."""
+    h = wl.muon_hp
+    if not (h.normuon or h.muon_plus):
+        return {}
+    es = 2 if h.ns_dtype == "bf16" else 4
+    wide = sum(m * n * es for (_, _, _, m, n) in wl.matrices() if m <= n)
+    tall = sum(m * n * es for (_, _, _, m, n) in wl.matrices() if m > n)
+    if h.muon_plus:
+        return {"rowsum": wide + tall, "colsum": wide + tall}
+    return {"rowsum": wide, "colsum": tall}
+
+
+def single_matrix_latency(stream, reps=200):
+    """Step time of the single fp32 256x128 matrix with fp32 Newton-Schulz (a
+    latency-bound step of 18 launches), timed with events over `reps` steps."""
+    import torch
+    import muon_adamw_amd as ma
+    import workloads
+    wl = workloads.workload(1)
+    d = workloads.generate(wl, device="cuda")
+    h = wl.muon_hp
+    hp = ma.muon_hparams(h.beta, h.nesterov, h.ns_steps, h.ns_coeffs, h.ns_eps, h.ns_dtype)
+    ps = [ma.MuonParam(t.param, t.grad, t.momentum, None, t.spec.views, t.spec.lr, t.spec.wd) for t in d.muon]
+    ws = torch.empty(ma.muon_workspace_bytes(ps, hp), dtype=torch.uint8, device="cuda")
+    for _ in range(10):
+        ma.muon_step(ps, hp, ws, stream)
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ev[0].record(stream)
+    for _ in range(reps):
+        ma.muon_step(ps, hp, ws, stream)
+    ev[1].record(stream)
+    torch.cuda.synchronize()
+    return {"step_us": round(ev[0].elapsed_time(ev[1]) / reps * 1e3, 2), "steps": reps}
+
+
 def cpu_baseline(wl, data, budget_s):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     whole Muon updates of the first matrices in tensor order until the time
@@ -125,9 +164,11 @@ def cpu_baseline(wl, data, budget_s):
     from oracle import storage
     try:
         from threadpoolctl import threadpool_info
-        threads = max([p.get("num_threads", 1) for p in threadpool_info()] or [os.cpu_count()])
+        pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()
+        threads = max([p.get("num_threads", 1) for p in pools] or [os.cpu_count()])
+        blas = ", ".join(sorted({f"{p.get('internal_api')} {p.get('version')}" for p in pools})) or "unknown"
     except Exception:  # pragma: no cover
-        threads = os.cpu_count()
+        threads, blas = os.cpu_count(), "unknown"
     h = wl.muon_hp
     hp = {"beta": h.beta, "nesterov": h.nesterov, "ns_steps": h.ns_steps, "ns_coeffs": h.ns_coeffs,
           "ns_eps": h.ns_eps, "normuon": h.normuon, "normuon_beta2": h.normuon_beta2,
@@ -151,9 +192,12 @@ def cpu_baseline(wl, data, budget_s):
         if spent >= budget_s:
             break
     total = len(wl.matrices())
+    all_flops = sum(ns_flops(min(m, n), max(m, n), h.ns_steps) for (_, _, _, m, n) in wl.matrices())
     return {"value": flops / spent / 1e12, "unit": "TFLOP/s", "cores": threads, "kind": "oracle",
             "sample": f"full fp64 Muon update of {nmat} of {total} matrices ({spent:.1f} s)",
-            "matrices_per_s": nmat / spent}
+            "matrices_per_s": nmat / spent, "os_cpu_count": os.cpu_count(), "blas": blas,
+            # the whole Muon half at the sample's rate (extrapolated from nmat of total matrices)
+            "muon_step_s_extrapolated": all_flops / (flops / spent)}
 
 
 def main():
@@ -214,6 +258,15 @@ def main():
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t_start) / args.steps
 
+    # host time of one muon_step call (binding + validation + cached plan +
+    # descriptor upload + launches; the device work is only enqueued)
+    host_s = []
+    for _ in range(args.steps):
+        t0 = time.perf_counter()
+        ma.muon_step(mparams, hp, ws, stream)
+        host_s.append(time.perf_counter() - t0)
+    torch.cuda.synchronize()
+
     # muon / adamw split with events on the step stream
     evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     for e in evs:
@@ -228,21 +281,30 @@ def main():
         hybrid_step()
     prof = ma.profile_end()
 
-    if args.calib_copy:
-        a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
-        b = torch.empty_like(a)
-        for _ in range(3):
-            b.copy_(a)
-        torch.cuda.synchronize()
-        del a, b
+    # measured ceiling of plain streaming: a 1 GiB device-to-device copy
+    # (torch's copy kernel), 2 GiB of traffic per copy
+    a = torch.empty(1 << 30, dtype=torch.uint8, device=dev)
+    b = torch.empty_like(a)
+    for _ in range(2 if args.calib_copy else 1):
+        b.copy_(a)
+    ce = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+    ce[0].record(stream)
+    for _ in range(5):
+        b.copy_(a)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    copy_gbps = 2 * (1 << 30) * 5 / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
+    del a, b
 
     nxt = None if args.no_next_rows else next_rows(data, aparams, ah, stream, args.profile_steps)
+    single = None if args.config == 1 or args.no_next_rows else single_matrix_latency(stream)
 
     mats = [(min(m, n), max(m, n)) for (_, _, _, m, n) in wl.matrices()]
     fl = ns_flops_per_launch(mats)
     fl["ns_persistent_bf16"] = ns_flops_persistent(mats, h.ns_steps)
     ns_total_flops = sum(ns_flops(r, c, h.ns_steps) for r, c in mats)
     by = elementwise_bytes(wl)
+    by_step = reduction_bytes(wl)
     kernels = {}
     for name, (launches, total_ms) in prof.items():
         avg_s = total_ms / launches / 1e3
@@ -255,6 +317,12 @@ def main():
         elif name in by:
             ach = by[name] / avg_s / 1e9
             k.update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s", frac=ach / HBM_PEAK_GBPS)
+        elif name in by_step:
+            # launches of one name differ in size: bytes of a step over its time
+            ach = by_step[name] / (total_ms / args.profile_steps / 1e3) / 1e9
+            k.update(bound="hbm", achieved=ach, peak=HBM_PEAK_GBPS, unit="GB/s", frac=ach / HBM_PEAK_GBPS)
+        else:
+            k.update(bound="latency")     # one small block per matrix, or a status word
         kernels[name] = k
     ns_kernel_s = sum(prof[n][1] for n in prof if n.startswith("ns_")) / args.profile_steps / 1e3
     dominant = max(prof, key=lambda n: prof[n][1])
@@ -292,9 +360,14 @@ def main():
         "adamw_GBps": round(by["adamw"] / (adam_ms / 1e3) / 1e9, 1) if aparams else None,
         "roofline": roofline,
         "kernels": kernels,
+        "host_us_per_muon_step": round(1e6 * sorted(host_s)[len(host_s) // 2], 1),
+        "copy_ceiling_GBps": round(copy_gbps, 1),
         "cpu_baseline": cpu,
         "next_rows": nxt,
+        "single_256x128_f32": single,
     }
+    if cpu is not None:
+        cpu["gpu_speedup_muon_step"] = round(cpu["muon_step_s_extrapolated"] / muon_s, 1)
     print(json.dumps(line), flush=True)
 
 

@@ -63,3 +63,24 @@ def test_cpu_baseline_times_the_oracle():
     assert out["kind"] == "oracle" and out["unit"] == "TFLOP/s"
     assert out["value"] > 0 and out["cores"] >= 1
     assert out["sample"].startswith("full fp64 Muon update of 1 of 1 matrices")
+
+
+def test_reduction_bytes_and_baseline_fields():
+    """One read of U per reduction pass: NorMuon (MoE set) reads the wide
+    matrices by canonical rows and the tall ones by canonical columns; Muon+
+    (wide-model set) reads every matrix in both passes. The baseline names its
+    BLAS, the host's core count and the whole Muon half's extrapolated time."""
+    import bench
+    import workloads
+    moe = workloads.workload(4)
+    gate_up = 64 * 2 * 1408 * 2048 * 2          # wide 1408x2048 views, bf16 U
+    down = 64 * 2048 * 1408 * 2                 # tall 2048x1408
+    assert bench.reduction_bytes(moe) == {"rowsum": gate_up, "colsum": down}
+    wide = workloads.workload(5)
+    every = sum(m * n * 2 for (_, _, _, m, n) in wide.matrices())
+    assert bench.reduction_bytes(wide) == {"rowsum": every, "colsum": every}
+    assert bench.reduction_bytes(workloads.workload(2)) == {}
+    wl = workloads.workload(1)
+    out = bench.cpu_baseline(wl, workloads.generate(wl, device="cpu"), 0.0)
+    assert out["os_cpu_count"] == os.cpu_count() and isinstance(out["blas"], str)
+    assert out["muon_step_s_extrapolated"] > 0
