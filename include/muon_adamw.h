@@ -334,6 +334,22 @@ ma_status ma_muon_matrix_info(const ma_muon_tensor* tensors, int32_t n, const ma
                               int32_t k, ma_matrix_info* info);
 
 /*
+ * Plan introspection: the task queues of the persistent Newton-Schulz launch
+ * (bf16 Newton-Schulz) for this tensor list, as the planner builds them.
+ * nseg (host, 8 entries, one per XCD) receives the number of segments in XCD
+ * x's queue, all 0 when the plan has none (fp32 Newton-Schulz, or no matrix).
+ * `segs` (host) receives up to `max_segs` records of 4 int32 {matrix,
+ * iteration * 4 + product (0 Gram, 1 square, 2 apply), index of the segment's
+ * first task in its queue, tiles of that matrix that must be complete before
+ * the segment's tiles start}, queue 0's first, in queue order. Host only:
+ * nothing is dereferenced on the device. MA_E_INVALID when nseg is NULL,
+ * max_segs < 0, or max_segs > 0 with segs NULL; otherwise the validation
+ * statuses of muon_step.
+ */
+ma_status ma_muon_queue_info(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
+                             int32_t* nseg, int32_t* segs, int32_t max_segs);
+
+/*
  * Per-kernel timing with HIP events, a profiling aid (not needed for use).
  * Between ma_profile_begin() and ma_profile_end() on one host thread, every
  * kernel that muon_step, ma_newton_schulz or adamw_step enqueues is bracketed

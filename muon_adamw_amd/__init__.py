@@ -79,7 +79,7 @@ class KernelTimeC(ctypes.Structure):
 EXPORTS = ("muon_step", "adamw_step", "ma_muon_workspace_bytes", "ma_last_error",
            "ma_newton_schulz", "ma_newton_schulz_workspace_bytes", "ma_muon_plan_counts",
            "ma_muon_matrix_info", "ma_profile_begin", "ma_profile_end", "ma_grad_norm_workspace_bytes",
-           "ma_global_grad_norm", "ma_muon_step_status")
+           "ma_global_grad_norm", "ma_muon_step_status", "ma_muon_queue_info")
 # bits of ma_muon_step_status
 NS_WAIT_TIMEOUT, NS_QUEUE_UNDRAINED = 1, 2
 
@@ -123,6 +123,9 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_global_grad_norm.restype = ctypes.c_int
     lib.ma_muon_step_status.argtypes = [P, ctypes.POINTER(I32), P]
     lib.ma_muon_step_status.restype = ctypes.c_int
+    lib.ma_muon_queue_info.argtypes = [ctypes.POINTER(MuonTensorC), I32, ctypes.POINTER(MuonHParamsC),
+                                       ctypes.POINTER(I32), ctypes.POINTER(I32), I32]
+    lib.ma_muon_queue_info.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -444,6 +447,23 @@ def matrix_info(tensors: Sequence[MuonParam], hp: MuonHParamsC, k: int) -> dict:
     info = MatrixInfoC()
     _check(lib.ma_muon_matrix_info(arr, len(tensors), ctypes.byref(hp), k, ctypes.byref(info)))
     return {f: getattr(info, f) for f, _ in MatrixInfoC._fields_ if f != "pad_"}
+
+
+def queue_info(tensors: Sequence[MuonParam], hp: MuonHParamsC):
+    """The persistent launch's task queues: a list of 8 lists (one per XCD)
+    of (matrix, iteration * 4 + product, first task, tiles required)."""
+    lib = load_library()
+    arr, _ = _muon_descs(tensors, check_device=False)
+    nseg = (ctypes.c_int32 * 8)()
+    _check(lib.ma_muon_queue_info(arr, len(tensors), ctypes.byref(hp), nseg, None, 0))
+    total = sum(nseg)
+    segs = (ctypes.c_int32 * max(4 * total, 1))()
+    _check(lib.ma_muon_queue_info(arr, len(tensors), ctypes.byref(hp), nseg, segs, total))
+    out, k = [], 0
+    for x in range(8):
+        out.append([tuple(segs[4 * (k + i): 4 * (k + i) + 4]) for i in range(nseg[x])])
+        k += nseg[x]
+    return out
 
 
 def workspace_u(workspace: torch.Tensor, info: dict, ns_dtype: str) -> torch.Tensor:

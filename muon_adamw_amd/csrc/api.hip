@@ -884,6 +884,24 @@ ma_status ma_muon_matrix_info(const ma_muon_tensor* tensors, int32_t n, const ma
   return MA_OK;
 }
 
+ma_status ma_muon_queue_info(const ma_muon_tensor* tensors, int32_t n, const ma_muon_hparams* hp,
+                             int32_t* nseg, int32_t* segs, int32_t max_segs) {
+  if (!nseg) return fail(MA_E_INVALID, "nseg is NULL");
+  if (max_segs < 0 || (max_segs > 0 && !segs)) return fail(MA_E_INVALID, "segs is NULL or max_segs is negative");
+  std::shared_ptr<const Plan> P;
+  ma_status st = get_plan(tensors, n, hp, false, P);
+  if (st != MA_OK) return st;
+  int32_t w = 0;
+  for (int x = 0; x < kXcds; ++x) {
+    nseg[x] = P->persist ? P->nseg[x] : 0;
+    if (!nseg[x]) continue;
+    const int32_t* rec = P->ints.data() + P->segs_off / sizeof(int32_t) + 4 * static_cast<size_t>(P->seg_off[x]);
+    for (int i = 0; i < nseg[x]; ++i, ++w)
+      if (w < max_segs) std::memcpy(segs + 4 * static_cast<size_t>(w), rec + 4 * i, 4 * sizeof(int32_t));
+  }
+  return MA_OK;
+}
+
 ma_status ma_profile_begin(void) {
   for (ProfRec& r : g_prof.recs) {
     g_prof.pool.push_back(r.e0);

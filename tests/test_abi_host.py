@@ -532,3 +532,78 @@ def test_grad_norm_partials_are_fp64(lib):
     g[0].grad, g[0].numel, g[0].dtype = BASE, 8192 * 100, ma.MA_F32
     g[1].grad, g[1].numel, g[1].dtype = BASE + (1 << 30), 8192 * 27 + 1, ma.MA_BF16
     assert lib.ma_grad_norm_workspace_bytes(g, 2) == 1024     # 128 partials x 8 bytes
+
+
+def queues(lib, arr, n, hp):
+    nseg = (ctypes.c_int32 * 8)()
+    assert lib.ma_muon_queue_info(arr, n, ctypes.byref(hp), nseg, None, 0) == 0
+    total = sum(nseg)
+    segs = (ctypes.c_int32 * max(4 * total, 1))()
+    assert lib.ma_muon_queue_info(arr, n, ctypes.byref(hp), nseg, segs, total) == 0
+    out, k = [], 0
+    for x in range(8):
+        out.append([tuple(segs[4 * (k + i): 4 * (k + i) + 4]) for i in range(nseg[x])])
+        k += nseg[x]
+    return out
+
+
+@pytest.mark.parametrize("k", [2, 3, 4, 5])
+def test_persistent_queues_are_deadlock_free_and_balanced(lib, k):
+    """The invariants the persistent launch's progress rests on, at the four
+    bf16 workloads: every matrix sits in one XCD's queue; a queue runs in
+    (iteration, product) order; the first task indices are the running tile
+    count; a segment's requirement is exactly the tiles of its matrix's
+    earlier products, all of which come earlier in the same queue (so a wait
+    only ever depends on tasks already handed out); XCD loads differ by at
+    most one matrix's work."""
+    wl = workloads.workload(k)
+    n = len(wl.muon)
+    hp = hp_of(wl)
+    arr = fake_descs(wl)
+    qs = queues(lib, arr, n, hp)
+    nmat = counts(lib, arr, n, hp)[1]
+    steps = hp.ns_steps
+
+    def tiles(kk):
+        i = info(lib, arr, n, hp, kk)
+        ntr, ntc = -(-i.rp // 256), -(-i.cp // 256)
+        tri = ntr * (ntr + 1) // 2
+        return (tri, tri, ntr * ntc), i
+
+    def work(kk, op):
+        t, i = tiles(kk)
+        return t[op] * (i.cp if op == 0 else i.rp)
+
+    home, loads = {}, []
+    for x, q in enumerate(qs):
+        start, last, done, load = 0, -1, {}, 0
+        for (m, itop, first, need) in q:
+            assert home.setdefault(m, x) == x, ("matrix on two XCDs", m)
+            assert itop >= last, ("queue order", x)
+            last = itop
+            it, op = itop >> 2, itop & 3
+            assert 0 <= it < steps and op in (0, 1, 2)
+            assert first == start
+            t, _ = tiles(m)
+            assert need == it * sum(t) + (t[0] if op >= 1 else 0) + (t[1] if op >= 2 else 0)
+            assert done.get(m, 0) == need, ("requirement not met by earlier segments", x, m, itop)
+            done[m] = done.get(m, 0) + t[op]
+            start += t[op]
+            load += work(m, op)
+        for m, d in done.items():
+            assert d == steps * sum(tiles(m)[0])
+        loads.append(load)
+    assert sorted(home) == list(range(nmat))
+    # the planner weighs a tile by its contraction length: padded columns for
+    # the Gram, padded rows for the square and the apply
+    biggest = max(sum(work(m, op) for op in range(3)) * steps for m in range(nmat))
+    assert max(loads) - min(loads) <= biggest
+
+
+def test_queue_info_is_empty_for_fp32_and_validates(lib):
+    wl = workloads.workload(1)
+    hp = hp_of(wl)
+    assert queues(lib, fake_descs(wl), 1, hp) == [[]] * 8
+    nseg = (ctypes.c_int32 * 8)()
+    assert lib.ma_muon_queue_info(fake_descs(wl), 1, ctypes.byref(hp), None, None, 0) == 1
+    assert lib.ma_muon_queue_info(fake_descs(wl), 1, ctypes.byref(hp), nseg, None, 4) == 1
