@@ -295,6 +295,15 @@ def main():
     torch.cuda.synchronize()
     copy_gbps = 2 * (1 << 30) * 5 / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
     del a, b
+    # measured ceiling of the bf16 matrix cores: the MFMA-only loop (no
+    # memory traffic), 1024 workgroups of 4 waves
+    sink = torch.empty(1024, dtype=torch.float32, device=dev)
+    ma.mfma_bf16_ceiling(sink, 1024, 100, stream)
+    ce[0].record(stream)
+    mfma_flops = ma.mfma_bf16_ceiling(sink, 1024, 1000, stream)
+    ce[1].record(stream)
+    torch.cuda.synchronize()
+    mfma_tflops = mfma_flops / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e12
 
     nxt = None if args.no_next_rows else next_rows(data, aparams, ah, stream, args.profile_steps)
     single = None if args.config == 1 or args.no_next_rows else single_matrix_latency(stream)
@@ -334,6 +343,10 @@ def main():
     traffic = counters.traffic_for(os.path.join(HERE, "profiles", f"counters_{wl.name}.json"), dominant)
     roofline = {"bound": dk.get("bound"), "achieved": dk.get("achieved"), "peak": dk.get("peak"),
                 "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": traffic, "kernel": dominant}
+    # the same achieved figure against the ceilings measured in this run
+    measured = {"mfma": mfma_tflops, "hbm": copy_gbps}.get(dk.get("bound"))
+    if measured and dk.get("achieved"):
+        roofline.update(peak_measured=round(measured, 1), frac_measured=dk["achieved"] / measured)
     muon_s = muon_ms / 1e3
     value = ns_total_flops / muon_s / 1e12
     line = {
@@ -362,6 +375,7 @@ def main():
         "kernels": kernels,
         "host_us_per_muon_step": round(1e6 * sorted(host_s)[len(host_s) // 2], 1),
         "copy_ceiling_GBps": round(copy_gbps, 1),
+        "mfma_ceiling_TFLOPs": round(mfma_tflops, 1),
         "cpu_baseline": cpu,
         "next_rows": nxt,
         "single_256x128_f32": single,

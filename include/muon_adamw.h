@@ -367,6 +367,18 @@ typedef struct {
 ma_status ma_profile_begin(void);
 int32_t ma_profile_end(ma_kernel_time* out, int32_t max);
 
+/*
+ * Measured ceiling of the bf16 matrix cores, a measurement aid beside the
+ * nominal peak (not needed for use). Enqueues on `stream` an MFMA-only loop
+ * with no memory traffic: `blocks` workgroups of 4 wave64s, each wave
+ * running `iters` rounds of 8 independent v_mfma_f32_32x32x16_bf16, i.e.
+ * blocks * 4 * iters * 8 * 32768 flops; the caller times it (events on the
+ * same stream). `sink` is a device array of `blocks` floats, written with one
+ * meaningless value per block. blocks in [1, 2^20], iters in [1, 2^24];
+ * MA_E_INVALID otherwise, with nothing enqueued.
+ */
+ma_status ma_mfma_bf16_ceiling(float* sink, int32_t blocks, int32_t iters, void* stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -79,7 +79,7 @@ class KernelTimeC(ctypes.Structure):
 EXPORTS = ("muon_step", "adamw_step", "ma_muon_workspace_bytes", "ma_last_error",
            "ma_newton_schulz", "ma_newton_schulz_workspace_bytes", "ma_muon_plan_counts",
            "ma_muon_matrix_info", "ma_profile_begin", "ma_profile_end", "ma_grad_norm_workspace_bytes",
-           "ma_global_grad_norm", "ma_muon_step_status", "ma_muon_queue_info")
+           "ma_global_grad_norm", "ma_muon_step_status", "ma_muon_queue_info", "ma_mfma_bf16_ceiling")
 # bits of ma_muon_step_status
 NS_WAIT_TIMEOUT, NS_QUEUE_UNDRAINED = 1, 2
 
@@ -126,6 +126,8 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_muon_queue_info.argtypes = [ctypes.POINTER(MuonTensorC), I32, ctypes.POINTER(MuonHParamsC),
                                        ctypes.POINTER(I32), ctypes.POINTER(I32), I32]
     lib.ma_muon_queue_info.restype = ctypes.c_int
+    lib.ma_mfma_bf16_ceiling.argtypes = [P, I32, I32, P]
+    lib.ma_mfma_bf16_ceiling.restype = ctypes.c_int
     _lib = lib
     return lib
 
@@ -474,6 +476,18 @@ def workspace_u(workspace: torch.Tensor, info: dict, ns_dtype: str) -> torch.Ten
     raw = workspace[info["u_offset"]: info["u_offset"] + nbytes]
     dt = torch.bfloat16 if ns_dtype == "bf16" else torch.float32
     return raw.view(dt).view(info["rp"], info["cp"])
+
+
+def mfma_bf16_ceiling(sink: torch.Tensor, blocks: int, iters: int, stream=None) -> int:
+    """Enqueues the MFMA-only loop (blocks x 4 waves x iters x 8 multiplies of
+    32768 flops); ``sink`` is a float32 GPU tensor of at least ``blocks``
+    entries. Returns the flop count; the caller times the launch."""
+    lib = load_library()
+    if not sink.is_cuda or sink.dtype != torch.float32 or sink.numel() < blocks or not sink.is_contiguous():
+        raise ValueError("sink must be a contiguous float32 GPU tensor of at least `blocks` entries")
+    _check(lib.ma_mfma_bf16_ceiling(ctypes.c_void_p(sink.data_ptr()), int(blocks), int(iters),
+                                    ctypes.c_void_p(_stream_handle(stream, sink.device))))
+    return blocks * 4 * iters * 8 * 32768
 
 
 def profile_begin():

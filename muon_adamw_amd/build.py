@@ -16,7 +16,7 @@ BUILD = os.path.join(HERE, "_build")
 LIB = os.path.join(HERE, "libmuon_adamw.so")
 
 SOURCES = ["api.hip", "k_momentum.hip", "k_ns_mfma.hip", "k_ns_f32.hip", "k_rowcol.hip",
-           "k_apply.hip", "k_adamw.hip", "k_gradnorm.hip"]
+           "k_apply.hip", "k_adamw.hip", "k_gradnorm.hip", "k_ceiling.hip"]
 
 ARCH = "gfx950"
 FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wshadow", "-Wno-unused-function",

@@ -902,6 +902,16 @@ ma_status ma_muon_queue_info(const ma_muon_tensor* tensors, int32_t n, const ma_
   return MA_OK;
 }
 
+ma_status ma_mfma_bf16_ceiling(float* sink, int32_t blocks, int32_t iters, void* stream) {
+  if (!sink) return fail(MA_E_INVALID, "sink is NULL");
+  if (blocks < 1 || blocks > (1 << 20)) return fail(MA_E_INVALID, "blocks must be in [1, 2^20]");
+  if (iters < 1 || iters > (1 << 24)) return fail(MA_E_INVALID, "iters must be in [1, 2^24]");
+  (void)hipGetLastError();
+  launch_mfma_ceiling(sink, blocks, iters, static_cast<hipStream_t>(stream));
+  if (hipGetLastError() != hipSuccess) return fail(MA_E_HIP, "ceiling kernel launch failed");
+  return MA_OK;
+}
+
 ma_status ma_profile_begin(void) {
   for (ProfRec& r : g_prof.recs) {
     g_prof.pool.push_back(r.e0);

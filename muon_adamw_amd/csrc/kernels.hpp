@@ -106,4 +106,9 @@ struct GradNormLaunch {
 void launch_grad_sumsq(const GradNormLaunch& L, int nblocks, hipStream_t s);
 void launch_grad_norm_finalize(const double* partial, int n, float max_norm, float* state, hipStream_t s);
 
+// Measured bf16 matrix-core ceiling: `blocks` workgroups of 4 waves, each
+// wave `iters` x 8 v_mfma_f32_32x32x16_bf16 on registers only (32768 flops
+// each); one float per block to `sink`.
+void launch_mfma_ceiling(float* sink, int blocks, int iters, hipStream_t s);
+
 }  // namespace ma

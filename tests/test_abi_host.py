@@ -607,3 +607,11 @@ def test_queue_info_is_empty_for_fp32_and_validates(lib):
     nseg = (ctypes.c_int32 * 8)()
     assert lib.ma_muon_queue_info(fake_descs(wl), 1, ctypes.byref(hp), None, None, 0) == 1
     assert lib.ma_muon_queue_info(fake_descs(wl), 1, ctypes.byref(hp), nseg, None, 4) == 1
+
+
+def test_mfma_ceiling_validation(lib):
+    """The measurement aid rejects its arguments before enqueueing anything."""
+    assert lib.ma_mfma_bf16_ceiling(None, 4, 10, None) == 1
+    assert lib.ma_mfma_bf16_ceiling(BASE, 0, 10, None) == 1
+    assert lib.ma_mfma_bf16_ceiling(BASE, 4, 0, None) == 1
+    assert lib.ma_mfma_bf16_ceiling(BASE, (1 << 20) + 1, 10, None) == 1
