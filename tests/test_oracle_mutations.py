@@ -423,3 +423,39 @@ def test_muon_plus_composition_mutants_caught(mutant, monkeypatch):
     monkeypatch.setattr(omuon, "matrix_update", mutant)
     with pytest.raises(AssertionError):
         pins.check_muon_plus_wrapper_step()
+
+
+# -- the MoE composition: Newton-Schulz -> NorMuon (V carried) -> scale -> wd mask --
+def _wd_mask_on_gradient(Q, W, G, V, hp, lr, wd):
+    """The decay mask decided against the raw gradient instead of the update.
+    (A mask on the Newton-Schulz output before NorMuon is no slip: NorMuon
+    scales each row by a positive factor and keeps every sign.)"""
+    m, n = Q.shape
+    U = omuon.newton_schulz(Q)
+    U_dir, V_new = omuon.normuon(U, V, hp.get("normuon_beta2", 0.95))
+    s = omuon.shape_scale(m, n)
+    keep = (G * W) >= 0.0
+    return W - lr * s * U_dir - lr * wd * np.where(keep, W, 0.0), V_new, U
+
+
+def _decay_scaled_by_shape(Q, W, G, V, hp, lr, wd):
+    """The shape scale multiplies the decay term too."""
+    m, n = Q.shape
+    U = omuon.newton_schulz(Q)
+    U_dir, V_new = omuon.normuon(U, V, hp.get("normuon_beta2", 0.95))
+    s = omuon.shape_scale(m, n)
+    return omuon.apply_cautious_wd(W, U_dir, lr, s * wd, s), V_new, U
+
+
+def test_normuon_state_not_carried_caught(monkeypatch):
+    plain = omuon.normuon
+    monkeypatch.setattr(omuon, "normuon", lambda U, V, beta2: plain(U, np.zeros_like(V), beta2))
+    with pytest.raises(AssertionError):
+        pins.check_normuon_wdmask_two_steps()
+
+
+@pytest.mark.parametrize("mutant", [_wd_mask_on_gradient, _decay_scaled_by_shape], ids=lambda f: f.__name__)
+def test_normuon_composition_mutants_caught(mutant, monkeypatch):
+    monkeypatch.setattr(omuon, "matrix_update", mutant)
+    with pytest.raises(AssertionError):
+        pins.check_normuon_wdmask_two_steps()

@@ -432,6 +432,58 @@ def test_muon_plus_and_wrapper_two_steps():
     check_muon_plus_wrapper_step()
 
 
+def check_normuon_wdmask_two_steps(step_fn=None):
+    """The MoE workload's composition over two steps, the second moment carried
+    from the first: Newton-Schulz (by SVD), NorMuon over each stored row, the
+    shape scale, then decay only where U*W >= 0 (flaxchat "Muon Algorithm",
+    steps 1 to 4; the shape scale from speedtronic "Muon update"). Batch 2 of a
+    packed tensor of two tall 12x5 views: the stored rows (12 per view) are not
+    the canonical rows (5), and sqrt(12/5) multiplies the update but not the
+    decay. The second gradient's rows are scaled unevenly so that its row means
+    differ from the first step's and the carried V matters."""
+    step_fn = step_fn or omuon.muon_tensor_step
+    r = rng(32)
+    lr, wd, b2 = 0.02, 0.1, 0.95
+    hp = dict(HP, normuon=True, normuon_beta2=b2, cautious="wd_mask")
+    batch, views, m, n = 2, 2, 12, 5
+    s = math.sqrt(m / n)
+    shape = (batch, views * m, n)
+    G1 = r.standard_normal(shape)
+    G2 = r.standard_normal(shape) * np.linspace(3.0, 0.2, views * m)[None, :, None]
+    W0 = 0.02 * r.standard_normal(shape)
+    V0 = np.zeros((batch, views * m))
+    W1, B1, V1, _ = step_fn(W0, G1, np.zeros(shape), V0, views, hp, lr, wd)
+    W2, _, V2, _ = step_fn(W1, G2, B1, V1, views, hp, lr, wd)
+    Q1 = 0.0975 * G1
+    Q2 = 0.045125 * G1 + 0.0975 * G2
+    carried = 0.0
+    for (Wprev, Wgot, Vprev, Vgot, Q) in [(W0, W1, V0, V1, Q1), (W1, W2, V1, V2, Q2)]:
+        masked = 0
+        for b in range(batch):
+            for v in range(views):
+                sl = slice(v * m, (v + 1) * m)
+                U = ns_by_svd(Q[b, sl])
+                rho = np.array([float(U[i] @ U[i]) / n for i in range(m)])
+                Vw = b2 * Vprev[b, sl] + (1.0 - b2) * rho
+                assert np.abs(Vgot[b, sl] - Vw).max() < 1e-15
+                carried = max(carried, float(np.abs(Vw - (1.0 - b2) * rho).max()))
+                Un = U / np.sqrt(Vw)[:, None]
+                Un *= np.linalg.norm(U) / np.linalg.norm(Un)
+                Wv = Wprev[b, sl]
+                prod = Un * Wv
+                assert np.abs(prod).min() > 1e-12          # no tie near the decision
+                keep = prod >= 0
+                masked += int(np.sum(~keep))
+                want = Wv - lr * s * Un - lr * wd * np.where(keep, Wv, 0.0)
+                assert np.abs(Wgot[b, sl] - want).max() < 1e-14, (b, v)
+        assert masked > 0
+    assert carried > 1e-3
+
+
+def test_normuon_wdmask_two_steps_tall_views():
+    check_normuon_wdmask_two_steps()
+
+
 # ---------------------------------------------------------------------------
 # AdamW closed forms
 # ---------------------------------------------------------------------------
