@@ -12,8 +12,9 @@
 - Gradients near the top of the fp32 range: the global norm clips instead of
   skipping, and Newton-Schulz stays finite and scale-free.
 - The wide-model workload's 28672 x 8192 bucket at full size, through
-  properties that hold at any size (the fp64 oracle of one such matrix takes
-  minutes of host time).
+  properties that hold at any size, and (last, marked slow) one such matrix
+  in the workload's full step against the oracle's whole chain (about 44
+  TFLOP of fp64 host arithmetic).
 
 Every expected value comes from the oracle run on the stored inputs, or from
 a closed property of the Newton-Schulz map.
@@ -156,14 +157,17 @@ def run_step_checked(wl, tol_ns, sample=None, update_tol=None):
     """One Muon step of workload `wl` on the GPU; its status; per matrix (all,
     or those `sample` picks): momentum at 1e-5, the oracle's whole chain for
     the Newton-Schulz output (localized bars at tol_ns), NorMuon's V (twice
-    tol_ns) and the stored parameters (check_update)."""
+    tol_ns) and the stored parameters (check_update). `sample` is a set of matrix indices
+    or a predicate on (index, matrix_info)."""
     h = hp_dict(wl.muon_hp)
     data = to_gpu(workloads.generate(wl, device="cpu" if wl.gen_device == "cpu" else DEV))
     params = muon_params(data)
     hp = hp_c(wl.muon_hp)
     nmat, _ = ma.plan_counts(params, hp)
     infos = [ma.matrix_info(params, hp, kk) for kk in range(nmat)]
-    sel = [kk for kk in range(nmat) if sample is None or kk in sample]
+    picked = sample if callable(sample) else (lambda kk, info: sample is None or kk in sample)
+    sel = [kk for kk in range(nmat) if picked(kk, infos[kk])]
+    assert sel, "no matrix picked"
     tens = sorted({infos[kk]["tensor"] for kk in sel})
     before = {ti: (data.muon[ti].param.clone(), data.muon[ti].momentum.clone(),
                    None if data.muon[ti].row_v is None else data.muon[ti].row_v.clone()) for ti in tens}
@@ -428,3 +432,17 @@ def test_wide_4L_d8192_tall_bucket_properties():
         for rows in (slice(0, 1024), slice(t.spec.rows - 1024, t.spec.rows)):
             B1 = omuon.momentum_ema(host(before[i][0][0, rows]), host(before[i][1][0, rows]), h["beta"])
             check_local(host(t.momentum[0, rows]), B1, 1e-5, (i, "momentum"))
+
+
+@pytest.mark.slow
+@pytest.mark.timeout(900)
+def test_wide_4L_d8192_up_projection_whole_chain():
+    """Layer 0's MLP up projection of the wide-model workload (28672 x 8192,
+    bf16, tall: the bucket that carries most of the step's Newton-Schulz
+    work), in the workload's full step, against the oracle's whole chain on
+    its stored inputs under the localized bars: momentum at 1e-5, the
+    Newton-Schulz output, then Muon+ row_col, the shape scale sqrt(3.5) and
+    the cautious wrapper on the stored bf16 parameters. The oracle's fp64
+    Newton-Schulz of this matrix is about 44 TFLOP of host arithmetic (one to
+    two minutes on 8 to 16 cores)."""
+    run_step_checked(workloads.workload(5), 2e-2, sample=lambda kk, info: info["tensor"] == 4)
