@@ -116,3 +116,61 @@ def to_gpu(data: workloads.WorkloadData, device="cuda"):
 
 def flush(msg):
     print(msg, flush=True)
+
+
+def bf16_spacing(v):
+    """Spacing of bf16 values at |v| (8 significant bits)."""
+    _, e = np.frexp(np.abs(np.asarray(v, dtype=np.float64)))
+    return np.where(v == 0, 2.0 ** -133, np.ldexp(1.0, e - 8))
+
+
+def check_update(W_gpu, W0, W_want, G, U_dir, h, lr, wd, s, param_dtype, tol, tol_ns):
+    """The stored parameters against the oracle's.
+
+    A cautious mask is a decision on the update direction, which the two
+    sides compute to different precision: an element may take the other
+    branch only where the oracle's own margin is inside the direction's
+    element bar (6 tol_ns of the RMS update), and then it equals that branch
+    (both branches rounded to the parameter dtype; where they round alike
+    there is nothing to tell). At most 3% of elements flip with bf16
+    Newton-Schulz, 0.1% with fp32.
+
+    fp32 parameters: the update W - W0 within `tol` of the oracle's, under
+    the localized bars. bf16 parameters: every element within one bf16
+    spacing of the oracle's rounded value plus the update's element bar (6
+    tol of its RMS plus its own size); with bf16 Newton-Schulz also the
+    update within `tol` (relative Frobenius); with fp32 Newton-Schulz at most
+    0.1% of the elements one spacing off (there one straddled rounding
+    boundary moves a whole bf16 spacing, a large relative error on an update
+    of a few spacings, so the Frobenius measure says nothing)."""
+    lr_s_U = lr * s * U_dir
+    band = 6 * tol_ns * np.sqrt(np.mean(lr_s_U * lr_s_U))
+    if h["cautious"] == "wd_mask":
+        alt = W0 - lr_s_U - lr * wd * np.where((U_dir * W0) >= 0.0, 0.0, W0)
+        near = np.abs(lr_s_U) < band
+    elif h["cautious"] == "wrapper":
+        delta = lr * wd * W0 + lr_s_U
+        alt = np.where((delta * G) > 0.0, W0, W0 - delta)
+        near = np.abs(delta) < band
+    else:
+        alt, near = W_want, np.zeros(W_want.shape, dtype=bool)
+    rounded = lambda x: storage.decode(storage.round_to(x, param_dtype), param_dtype)
+    R_want, R_alt = rounded(W_want), rounded(alt)
+    flipped = near & (np.abs(W_gpu - R_alt) < np.abs(W_gpu - R_want))
+    loose = tol_ns > 1e-3
+    assert flipped.mean() <= (0.03 if loose else 1e-3), ("mask flips", float(flipped.mean()))
+    exact = np.where(flipped, alt, W_want)
+    W_ref = np.where(flipped, R_alt, R_want)
+    if param_dtype == "bf16":
+        dW = exact - W0
+        allowed = bf16_spacing(W_ref) + 6 * tol * (np.sqrt(np.mean(dW * dW)) + np.abs(dW))
+        worst = (np.abs(W_gpu - W_ref) / allowed).max()
+        assert worst <= 1.0, ("bf16 element", float(worst))
+        if loose:
+            e = np.linalg.norm((W_gpu - W0) - (W_ref - W0)) / np.linalg.norm(W_ref - W0)
+            assert e < tol, ("update", e)
+        else:
+            share = float((W_gpu != W_ref).mean())
+            assert share <= 1e-3, ("bf16 spacing share", share)
+    else:
+        check_local(W_gpu - W0, W_ref - W0, tol, "update")
