@@ -257,6 +257,13 @@ def main():
         hybrid_step()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t_start) / args.steps
+    # device status of the last timed step (outside the timed region): 0, or
+    # the persistent launch's safeguard bits, in which case its results and
+    # therefore this line are not to be trusted
+    ns_status = ma.muon_step_status(ws, stream)
+    if ns_status:
+        print(f"warning: muon_step status {ns_status} (a bounded wait ran out or a queue was not drained)",
+              file=sys.stderr, flush=True)
 
     # host time of one muon_step call (binding + validation + cached plan +
     # descriptor upload + launches; the device work is only enqueued)
@@ -373,6 +380,7 @@ def main():
         "adamw_GBps": round(by["adamw"] / (adam_ms / 1e3) / 1e9, 1) if aparams else None,
         "roofline": roofline,
         "kernels": kernels,
+        "ns_status": ns_status,
         "host_us_per_muon_step": round(1e6 * sorted(host_s)[len(host_s) // 2], 1),
         "copy_ceiling_GBps": round(copy_gbps, 1),
         "mfma_ceiling_TFLOPs": round(mfma_tflops, 1),
