@@ -447,6 +447,49 @@ def test_matrix_expansion_matches_the_oracle_on_random_lists(lib):
         assert nb == len(buckets)
 
 
+def test_plan_cache_and_errors_are_thread_safe(lib):
+    """Host calls from eight threads at once (ctypes releases the GIL during a
+    foreign call): 100 tensor-list structures, more than the plan cache keeps
+    (64), so it is cleared while other threads still use plans taken from it.
+    Every workspace size equals the single-threaded answer, and a thread that
+    makes an invalid call reads its own message from ma_last_error."""
+    import threading
+    rng = np.random.default_rng(5)
+    hp = ma.muon_hparams(ns_dtype="bf16")
+
+    def one(batch, rows, cols, views):
+        arr = (ma.MuonTensorC * 1)()
+        arr[0].param, arr[0].grad, arr[0].momentum = BASE, BASE + (1 << 36), BASE + (2 << 36)
+        arr[0].batch, arr[0].rows, arr[0].cols, arr[0].views = batch, rows, cols, views
+        arr[0].param_dtype = arr[0].grad_dtype = ma.MA_F32
+        arr[0].lr, arr[0].weight_decay = 0.02, 0.1
+        return arr
+
+    structs = [one(1 + k % 3, int(rng.integers(1, 700)), int(rng.integers(1, 700)), 1) for k in range(100)]
+    want = [lib.ma_muon_workspace_bytes(a, 1, ctypes.byref(hp)) for a in structs]
+    assert all(w > 0 for w in want)
+    bad = one(1, 30, 40, 7)                             # 7 does not divide 30
+    problems = []
+
+    def work(tid):
+        r = np.random.default_rng(100 + tid)
+        for it in range(400):
+            k = int(r.integers(0, len(structs)))
+            got = lib.ma_muon_workspace_bytes(structs[k], 1, ctypes.byref(hp))
+            if got != want[k]:
+                problems.append((tid, k, got, want[k]))
+            if it % 40 == tid % 40:
+                if lib.ma_muon_workspace_bytes(bad, 1, ctypes.byref(hp)) != 0 or b"views" not in lib.ma_last_error():
+                    problems.append((tid, "error message", lib.ma_last_error()))
+
+    threads = [threading.Thread(target=work, args=(t,)) for t in range(8)]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert not problems, problems[:5]
+
+
 def test_plan_cache_still_validates_every_call(lib):
     """A cached plan skips the planning, never the validation: the same
     structure with a misaligned or an aliased pointer is still rejected."""
