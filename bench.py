@@ -45,6 +45,20 @@ def ns_flops(r, c, steps):
     return steps * (r * (r + 1) * c + r * (r + 1) * r + 2 * r * r * c)
 
 
+def ns_flops_dense(r, c, steps):
+    """Dense-equivalent FLOPs of Newton-Schulz: the full Gram (2 r^2 c), the
+    full square (2 r^3) and B X (2 r^2 c). A label for comparison with dense
+    GEMM counts; the achieved figures use ns_flops."""
+    return steps * (4 * r * r * c + 2 * r ** 3)
+
+
+def ns_flop_per_step(mats, steps):
+    """Newton-Schulz FLOPs of one step, algorithmic (as computed) and
+    dense-equivalent, over canonical (r, c) shapes."""
+    return {"algorithmic": sum(ns_flops(r, c, steps) for r, c in mats),
+            "dense_equivalent": sum(ns_flops_dense(r, c, steps) for r, c in mats)}
+
+
 def ns_flops_per_launch(mats):
     """Algorithmic FLOPs of one launch of each Newton-Schulz product."""
     gram = sum(r * (r + 1) * c for r, c in mats)
@@ -375,6 +389,7 @@ def main():
         "muon_step_ms": round(muon_ms, 4),
         "adamw_step_ms": round(adam_ms, 4),
         "matrices_per_s": round(len(mats) / muon_s, 1),
+        "ns_flop_per_step": ns_flop_per_step(mats, h.ns_steps),
         "ns_tflops_kernels": round(ns_total_flops / ns_kernel_s / 1e12, 3),
         "ns_frac_of_bf16_peak": round(ns_total_flops / ns_kernel_s / 1e12 / BF16_PEAK_TFLOPS, 4),
         "adamw_GBps": round(by["adamw"] / (adam_ms / 1e3) / 1e9, 1) if aparams else None,

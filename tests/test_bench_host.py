@@ -53,6 +53,22 @@ def test_algorithmic_units():
     assert abs(b["momentum"] / 1e9 - 1.19) < 0.01 and abs(b["adamw"] / 1e9 - 1.08) < 0.01
 
 
+def test_flop_counts_per_step():
+    """Newton-Schulz FLOPs of a whole step on the d768 set: dense-equivalent
+    1.6307 TF (full Gram, full square, B X), algorithmic 1.1422 TF (one
+    triangle for the Gram and the square, as computed), both over 72 matrices
+    (48 of 768 x 768, 24 of 768 x 3072 in canonical orientation)."""
+    import bench
+    import workloads
+    wl = workloads.workload(2)
+    mats = [(min(m, n), max(m, n)) for (_, _, _, m, n) in wl.matrices()]
+    assert sorted(set(mats)) == [(768, 768), (768, 3072)] and len(mats) == 72
+    f = bench.ns_flop_per_step(mats, 5)
+    assert abs(f["dense_equivalent"] / 1.6307e12 - 1) < 1e-4, f
+    assert abs(f["algorithmic"] / 1.1422e12 - 1) < 1e-4, f
+    assert f["algorithmic"] < f["dense_equivalent"]
+
+
 def test_cpu_baseline_times_the_oracle():
     """The cpu_baseline leg on the small single-matrix set, on the host: the
     oracle timed on a bounded sample, reported in the GPU figure's unit."""
