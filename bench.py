@@ -317,11 +317,13 @@ def main():
     copy_gbps = 2 * (1 << 30) * 5 / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e9
     del a, b
     # measured ceiling of the bf16 matrix cores: the MFMA-only loop (no
-    # memory traffic), 1024 workgroups of 4 waves
-    sink = torch.empty(1024, dtype=torch.float32, device=dev)
-    ma.mfma_bf16_ceiling(sink, 1024, 100, stream)
+    # memory traffic), 1024 workgroups of 4 waves; the counter summary
+    # calibrates its MFMA-op counter on the same launch
+    from muon_adamw_amd import counters
+    sink = torch.empty(counters.CEILING_BLOCKS, dtype=torch.float32, device=dev)
+    ma.mfma_bf16_ceiling(sink, counters.CEILING_BLOCKS, counters.CEILING_ITERS // 10, stream)
     ce[0].record(stream)
-    mfma_flops = ma.mfma_bf16_ceiling(sink, 1024, 1000, stream)
+    mfma_flops = ma.mfma_bf16_ceiling(sink, counters.CEILING_BLOCKS, counters.CEILING_ITERS, stream)
     ce[1].record(stream)
     torch.cuda.synchronize()
     mfma_tflops = mfma_flops / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e12
@@ -360,10 +362,15 @@ def main():
     # HBM bytes per launch from the committed counter summary of this
     # workload (FETCH_SIZE/WRITE_SIZE passes, copy-calibrated), while the
     # kernel sources are unchanged since it was taken
-    from muon_adamw_amd import counters
-    traffic = counters.traffic_for(os.path.join(HERE, "profiles", f"counters_{wl.name}.json"), dominant)
+    summary = os.path.join(HERE, "profiles", f"counters_{wl.name}.json")
+    traffic = counters.traffic_for(summary, dominant)
     roofline = {"bound": dk.get("bound"), "achieved": dk.get("achieved"), "peak": dk.get("peak"),
                 "unit": dk.get("unit"), "frac": dk.get("frac"), "traffic": traffic, "kernel": dominant}
+    # flops the matrix cores executed per launch (MFMA-op counter, calibrated
+    # on the ceiling loop), beside the algorithmic flops the rate divides
+    counted = counters.flops_for(summary, dominant) if dk.get("bound") == "mfma" else None
+    if counted:
+        roofline.update(flops_counted=counted, flops_algorithmic=fl.get(dominant))
     # the same achieved figure against the ceilings measured in this run
     measured = {"mfma": mfma_tflops, "hbm": copy_gbps}.get(dk.get("bound"))
     if measured and dk.get("achieved"):
