@@ -113,6 +113,12 @@ def next_rows(data, aparams, ah, stream, reps):
     return out
 
 
+def progress(msg):
+    """One line per finished phase on stderr (a long profiled run shows it is
+    alive; the JSON line on stdout stays the only result)."""
+    print(f"# {msg}", file=sys.stderr, flush=True)
+
+
 def elementwise_bytes(wl):
     """Algorithmic HBM bytes of one launch of each elementwise kernel."""
     es = {"f32": 4, "bf16": 2}
@@ -264,6 +270,7 @@ def main():
     for _ in range(args.warmup):
         hybrid_step()
     torch.cuda.synchronize()
+    progress(f"{args.warmup} warm-up steps done")
 
     # whole-step timing
     t_start = time.perf_counter()
@@ -271,6 +278,7 @@ def main():
         hybrid_step()
     torch.cuda.synchronize()
     wall = (time.perf_counter() - t_start) / args.steps
+    progress(f"{args.steps} timed steps: {wall * 1e3:.3f} ms each")
     # device status of the last timed step (outside the timed region): 0, or
     # the persistent launch's safeguard bits, in which case its results and
     # therefore this line are not to be trusted
@@ -295,12 +303,14 @@ def main():
     torch.cuda.synchronize()
     muon_ms = sum(e[0].elapsed_time(e[1]) for e in evs) / len(evs)
     adam_ms = sum(e[1].elapsed_time(e[2]) for e in evs) / len(evs)
+    progress(f"event split: muon_step {muon_ms:.3f} ms, adamw_step {adam_ms:.3f} ms")
 
     # per-kernel HIP-event timing (separate pass: events add gaps)
     ma.profile_begin()
     for _ in range(args.profile_steps):
         hybrid_step()
     prof = ma.profile_end()
+    progress("per-kernel timing pass done")
 
     # measured ceiling of plain streaming: a 1 GiB device-to-device copy
     # (torch's copy kernel), 2 GiB of traffic per copy
@@ -327,6 +337,7 @@ def main():
     ce[1].record(stream)
     torch.cuda.synchronize()
     mfma_tflops = mfma_flops / (ce[0].elapsed_time(ce[1]) / 1e3) / 1e12
+    progress(f"ceilings: copy {copy_gbps:.0f} GB/s, MFMA loop {mfma_tflops:.0f} TFLOP/s")
 
     nxt = None if args.no_next_rows else next_rows(data, aparams, ah, stream, args.profile_steps)
     single = None if args.config == 1 or args.no_next_rows else single_matrix_latency(stream)
