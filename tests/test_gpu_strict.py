@@ -385,6 +385,40 @@ def test_wide_4L_d8192_tall_bucket_properties():
             check_local(host(t.momentum[0, rows]), B1, 1e-5, (i, "momentum"))
 
 
+# ---------------------------------------------------------------------------
+# At the planner's limits
+# ---------------------------------------------------------------------------
+@pytest.mark.parametrize("dt", ["f32", "bf16"])
+@pytest.mark.parametrize("shape", [(65536, 129), (129, 65536)], ids=["tall", "wide"])
+def test_newton_schulz_at_the_largest_dimension(shape, dt):
+    """The largest dimension the planner accepts (65536) beside a ragged one:
+    canonical 129 x 65536, padded to 256 x 65536, a contraction of 65536 in
+    the Gram and one row of 256 APPLY tiles; against the oracle under the
+    localized bars (fp32 1e-5: the aspect ratio is 508; bf16 2e-2)."""
+    flush(f"ns largest dimension {shape} {dt}")
+    x = randn(shape, 900 + shape[0] % 7)
+    if dt == "bf16":
+        x = x.to(torch.bfloat16)
+    out = ns_with_status(x.to(DEV), ma.muon_hparams(ns_dtype=dt))
+    want = omuon.newton_schulz(x.double().numpy())
+    check_local(out.cpu().double().numpy(), want, 1e-5 if dt == "f32" else 2e-2, (shape, dt))
+
+
+def test_step_with_more_matrices_than_the_persistent_queues_take():
+    """70000 batched 64 x 64 matrices, more than the 65536 the persistent
+    launch's queues are built for: the step takes the per-launch schedule
+    over 70000-tile launches; status 0; momentum, the
+    Newton-Schulz output and the updated parameters of 66 matrices spread
+    over the batch (every 1111th, the second and the last) against the
+    oracle."""
+    # square: the emulated bf16 chain stays under 0.015 of the oracle at
+    # 64 x 64 (tall 16 x 4 matrices reach 0.06, too few elements to average)
+    spec = workloads.MuonTensorSpec("many", 70000, 64, 64, grad_std=1.0)
+    wl = workloads.Workload("many_64x64", 51, (spec,), (), workloads.MuonHParams(ns_dtype="bf16"))
+    sample = set(range(0, 70000, 1111)) | {1, 69999}
+    run_step_checked(wl, 2e-2, sample=sample)
+
+
 @pytest.mark.slow
 @pytest.mark.timeout(900)
 def test_wide_4L_d8192_up_projection_whole_chain():
