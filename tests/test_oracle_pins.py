@@ -85,6 +85,18 @@ def test_ns_scalar_constants():
     f = phi_iter((1 / math.sqrt(3)) * math.sqrt(3) / (math.sqrt(3) + EPS))
     assert abs(f - 0.6857849207555402) < 1e-6
     assert np.abs(got - f * Q).max() < 1e-13
+    # 5x2 with orthonormal columns (tall, transposed inside): both normalised
+    # singular values are 1/sqrt(2)
+    Q, _ = np.linalg.qr(rng(4).standard_normal((5, 2)))
+    f = phi_iter(math.sqrt(2) / (math.sqrt(2) + EPS) / math.sqrt(2))
+    assert abs(f - 1.1081111156829304) < 1e-6
+    assert np.abs(omuon.newton_schulz(Q) - f * Q).max() < 1e-13
+    # 4x4 orthogonal (square, not transposed): every normalised singular value
+    # is 1/2
+    Q, _ = np.linalg.qr(rng(6).standard_normal((4, 4)))
+    f = phi_iter(2.0 / (2.0 + EPS) / 2.0)
+    assert abs(f - 0.7654385304543396) < 1e-6
+    assert np.abs(omuon.newton_schulz(Q) - f * Q).max() < 1e-13
 
 
 def test_ns_transpose_symmetry():
