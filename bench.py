@@ -223,8 +223,9 @@ def cpu_baseline(wl, data, budget_s):
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this build "
-              "(the multi-GPU sharding is a design, not an implementation).", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported: the library "
+              "has no multi-GPU path (the sharding across GPUs is a design, not an implementation).",
+              file=sys.stderr)
         sys.exit(2)
     import torch
     import muon_adamw_amd as ma

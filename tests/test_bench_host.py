@@ -1,5 +1,5 @@
 """bench.py on a host without a GPU: more than one GPU is refused with a
-message (this build runs on one GPU), without a visible GPU the bench fails
+message (the library runs on one GPU), without a visible GPU the bench fails
 loudly instead of falling back to anything, and its algorithmic units and
 cpu_baseline leg give the figures the roofline and the baseline report."""
 import os
