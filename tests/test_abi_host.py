@@ -197,6 +197,54 @@ def test_workspace_bytes_cover_buffers(lib):
     assert last.u_offset + last.rp * last.cp * 2 <= need
 
 
+@pytest.mark.parametrize("seed", range(12))
+def test_workspace_buffers_are_disjoint_and_aligned(lib, seed):
+    """Random tensor lists (views, batches, ragged and tall shapes, both NS
+    dtypes): every matrix's two X buffers, A and B lie past the header, inside
+    the workspace, 256-byte aligned and disjoint from every other matrix's.
+    The final output lands in the second X buffer after an odd step count and
+    in the first after an even one, so plans for 5 and 4 steps give both X
+    offsets: the step count only changes the size of the tables at the front
+    (queue segments, coefficients), which shifts every buffer by the same
+    amount, the difference of the two workspace sizes (checked on A and B)."""
+    r = np.random.default_rng(1000 + seed)
+    nt = int(r.integers(1, 6))
+    arr = (ma.MuonTensorC * nt)()
+    addr = BASE
+    for i in range(nt):
+        views = int(r.choice([1, 1, 2, 3]))
+        rows, cols, batch = views * int(r.integers(1, 400)), int(r.integers(1, 900)), int(r.integers(1, 4))
+        d = arr[i]
+        n = batch * rows * cols
+        d.param = addr; addr += n * 4 + (1 << 30)
+        d.grad = None if r.random() < 0.15 else addr; addr += n * 4 + (1 << 30)
+        d.momentum = addr; addr += n * 4 + (1 << 30)
+        d.batch, d.rows, d.cols, d.views = batch, rows, cols, views
+        d.param_dtype = d.grad_dtype = ma.MA_F32
+        d.lr, d.weight_decay = 0.02, 0.1
+    for ns_dtype, es in (("bf16", 2), ("f32", 4)):
+        hp5, hp4 = ma.muon_hparams(ns_dtype=ns_dtype, ns_steps=5), ma.muon_hparams(ns_dtype=ns_dtype, ns_steps=4)
+        ws = lib.ma_muon_workspace_bytes(arr, nt, ctypes.byref(hp5))
+        shift = ws - lib.ma_muon_workspace_bytes(arr, nt, ctypes.byref(hp4))
+        assert shift >= 0 and shift % 256 == 0
+        nm = ctypes.c_int32(0)
+        assert lib.ma_muon_plan_counts(arr, nt, ctypes.byref(hp5), ctypes.byref(nm), None) == 0
+        if nm.value == 0:
+            assert ws == 0
+            continue
+        ranges = []
+        for k in range(nm.value):
+            i5, i4 = info(lib, arr, nt, hp5, k), info(lib, arr, nt, hp4, k)
+            assert (i5.a_offset, i5.b_offset) == (i4.a_offset + shift, i4.b_offset + shift)
+            xb, ab = i5.rp * i5.cp * es, i5.rp * i5.rp * es
+            for off, size in ((i4.u_offset + shift, xb), (i5.u_offset, xb), (i5.a_offset, ab), (i5.b_offset, ab)):
+                assert off % 256 == 0 and off >= 256 and off + size <= ws, (k, off, size, ws)
+                ranges.append((off, off + size, k))
+        ranges.sort()
+        for (lo0, hi0, k0), (lo1, hi1, k1) in zip(ranges, ranges[1:]):
+            assert hi0 <= lo1, ("overlap", k0, k1, (lo0, hi0), (lo1, hi1))
+
+
 def step(lib, arr, n, hp, ws=None, nbytes=0):
     return lib.muon_step(arr, n, ctypes.byref(hp), ws, nbytes, None)
 
