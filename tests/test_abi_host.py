@@ -245,6 +245,50 @@ def test_workspace_buffers_are_disjoint_and_aligned(lib, seed):
             assert hi0 <= lo1, ("overlap", k0, k1, (lo0, hi0), (lo1, hi1))
 
 
+@pytest.mark.parametrize("seed", range(8))
+def test_alias_check_against_a_reference(lib, seed):
+    """Random placements of parameters, momenta and NorMuon second moments,
+    many of them touching or overlapping: the library reports MA_E_ALIAS
+    exactly when some two byte ranges [start, start + size) intersect
+    (gradients are read only and may be shared; tensors without a gradient
+    are not stepped and are not checked)."""
+    r = np.random.default_rng(2000 + seed)
+    hp = ma.muon_hparams(ns_dtype="bf16", normuon=True)
+    for trial in range(60):
+        nt = int(r.integers(2, 5))
+        arr = (ma.MuonTensorC * nt)()
+        ranges = []
+        for i in range(nt):
+            d = arr[i]
+            rows, cols = 2 * int(r.integers(1, 8)), int(r.integers(1, 8))
+            d.batch, d.rows, d.cols, d.views = 1, rows, cols, 2
+            d.param_dtype = d.grad_dtype = ma.MA_F32
+            d.lr, d.weight_decay = 0.02, 0.1
+            n = rows * cols
+            # addresses on a small grid (even trials: ranges nearly always
+            # touch or overlap) or a wider one (odd trials: often disjoint)
+            span = 200 if trial % 2 == 0 else 20000
+            pick = lambda: BASE + 4 * int(r.integers(0, span))
+            d.param, d.momentum, d.row_v = pick(), pick(), pick()
+            d.grad = BASE + (1 << 34)
+            live = r.random() > 0.1
+            if not live:
+                d.grad = None
+            if live:
+                ranges += [(d.param, d.param + 4 * n), (d.momentum, d.momentum + 4 * n),
+                           (d.row_v, d.row_v + 4 * rows)]
+        ranges.sort()
+        overlap = any(a[1] > b[0] for a, b in zip(ranges, ranges[1:]))
+        st = lib.ma_muon_workspace_bytes(arr, nt, ctypes.byref(hp))
+        err = lib.ma_last_error().decode() if st == 0 else ""
+        if not ranges:                       # nothing to step: 0, and no new error
+            assert st == 0
+        elif overlap:
+            assert st == 0 and "overlapping" in err, (trial, ranges)
+        else:
+            assert st > 0, (trial, err)
+
+
 def step(lib, arr, n, hp, ws=None, nbytes=0):
     return lib.muon_step(arr, n, ctypes.byref(hp), ws, nbytes, None)
 
