@@ -394,14 +394,18 @@ def test_newton_schulz_at_the_largest_dimension(shape, dt):
     """The largest dimension the planner accepts (65536) beside a ragged one:
     canonical 129 x 65536, padded to 256 x 65536, a contraction of 65536 in
     the Gram and one row of 256 APPLY tiles; against the oracle under the
-    localized bars (fp32 1e-5: the aspect ratio is 508; bf16 2e-2)."""
+    localized bars. bf16: 2e-2. fp32: 1e-4, not 1e-5: each thread of the fp32
+    Gram adds its 65536 products one fp32 FMA after another, and such a sum
+    carries a relative error of about u sqrt(K) / sqrt(3) ~ 9e-6 (u = 2^-24);
+    emulated exactly that way, the whole chain lands at 1.8e-5 (rows 4.1e-5)
+    of the fp64 oracle."""
     flush(f"ns largest dimension {shape} {dt}")
     x = randn(shape, 900 + shape[0] % 7)
     if dt == "bf16":
         x = x.to(torch.bfloat16)
     out = ns_with_status(x.to(DEV), ma.muon_hparams(ns_dtype=dt))
     want = omuon.newton_schulz(x.double().numpy())
-    check_local(out.cpu().double().numpy(), want, 1e-5 if dt == "f32" else 2e-2, (shape, dt))
+    check_local(out.cpu().double().numpy(), want, 1e-4 if dt == "f32" else 2e-2, (shape, dt))
 
 
 def test_step_with_more_matrices_than_the_persistent_queues_take():
