@@ -9,9 +9,11 @@
  *
  * Errors: every entry point validates all of its arguments before it enqueues
  * anything, so a non-OK status leaves every buffer untouched (the hybrid step
- * is all-or-nothing, as the kimi-k3 "Optimization" chapter requires when an
- * FP16 overflow skips "the whole hybrid optimizer update"). ma_last_error()
- * returns a thread-local message for the last non-OK status. Kernel faults are
+ * is all-or-nothing: the kimi-k3 "Optimization" chapter has an FP16 overflow
+ * skip the update of both optimizers together). ma_last_error() returns a
+ * thread-local message for the last non-OK status; the pointer stays valid
+ * until this thread's next call that fails, so read it after the call returns
+ * and copy it to keep it. Kernel faults are
  * asynchronous and surface at the caller's next synchronisation; a launch
  * failure seen right after enqueueing returns MA_E_HIP.
  *
@@ -228,8 +230,8 @@ typedef struct {
  * p <- p - lr * ( (m/(1-beta1^step)) / (sqrt(v/(1-beta2^step)) + eps) + wd p ).
  * step >= 1 counts successful updates (the caller's host counter; a step the
  * clip state skipped is not one).
- * cautious   MA_CAUTIOUS_WRAPPER (speedtronic "Cautious updates": "cautious
- *            composes with either base optimizer") keeps an entry's observed
+ * cautious   MA_CAUTIOUS_WRAPPER (speedtronic "Cautious updates": the wrapper
+ *            applies to either base optimizer) keeps an entry's observed
  *            update, decay included, only where update * g > 0 and leaves the
  *            parameter as it was elsewhere; m and v are updated either way.
  *            MA_CAUTIOUS_WD_MASK is Muon's rule: MA_E_UNSUPPORTED.

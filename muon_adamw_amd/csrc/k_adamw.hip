@@ -7,8 +7,8 @@
 //     global gradient norm before either optimizer; an overflow skips the
 //     whole hybrid update): g is read times the clip factor, and a skipped
 //     step writes nothing;
-//   * the cautious wrapper (speedtronic "Cautious updates"; "cautious
-//     composes with either base optimizer"): an entry keeps its observed
+//   * the cautious wrapper (speedtronic "Cautious updates": it applies to
+//     either base optimizer): an entry keeps its observed
 //     update, decay included, only where update * g > 0, else p is left as
 //     it was; m and v are always the base optimizer's;
 //   * bf16 moments (dew.training.optim "bf16_moments"): m and v are read,

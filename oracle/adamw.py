@@ -15,11 +15,11 @@ from . import storage
 def adamw_update(p, g, m, v, lr, wd, beta1, beta2, eps, step, cautious=False):
     """One AdamW step in float64; ``step`` counts successful updates from 1.
 
-    ``cautious``: the speedtronic "Cautious updates" wrapper over AdamW
-    ("cautious composes with either base optimizer"): the observed update
-    p - p_new, decay included, is kept only where it times the gradient is
-    > 0; elsewhere p stays as it was. The moments are the base optimizer's
-    either way ("native ... AdamW state remain intact")."""
+    ``cautious``: the speedtronic "Cautious updates" wrapper over AdamW (the
+    wrapper applies to either base optimizer): the observed update p - p_new,
+    decay included, is kept only where it times the gradient is > 0;
+    elsewhere p stays as it was. The moments are the base optimizer's either
+    way (the section leaves AdamW's own state untouched by the mask)."""
     m = beta1 * m + (1.0 - beta1) * g
     v = beta2 * v + (1.0 - beta2) * g * g
     m_hat = m / (1.0 - beta1 ** step)

@@ -60,8 +60,8 @@ def round_to(x, dtype: str) -> np.ndarray:
 
 
 # -- dew.training.optim "stochastic_round_bf16" -------------------------------
-# The pages name no hash ("a counter-based hash" of the seed and each element's
-# flat index). The one used is SplitMix64 (Steele, Lea and Flood, "Fast
+# The pages ask for a counter-based hash of the seed and each element's flat
+# index and name none. The one used is SplitMix64 (Steele, Lea and Flood, "Fast
 # splittable pseudorandom number generators", OOPSLA 2014): state advanced by
 # the golden-ratio increment, output function mix64 below.
 SPLITMIX_GAMMA = 0x9E3779B97F4A7C15

@@ -106,6 +106,83 @@ int main(void) {{
         assert int(got[k]) == v, (k, got[k], v)
 
 
+def test_a_c_caller_links_the_library_and_gets_the_same_answers(tmp_path, lib):
+    """The boundary from C, without Python: a program that includes the
+    header and links libmuon_adamw.so describes the GPT workload's first
+    layer (six tensors) with made-up device addresses, asks for the plan
+    counts, the workspace size and one matrix's layout, then makes two
+    invalid calls; every answer equals the binding's. Only host-side entry
+    points are called: nothing reaches the GPU."""
+    src = tmp_path / "caller.c"
+    src.write_text(f'''
+#include <stdio.h>
+#include <stdint.h>
+#include <string.h>
+#include "{HEADER}"
+int main(void) {{
+  const int64_t shapes[6][2] = {{{{768, 768}}, {{768, 768}}, {{768, 768}}, {{768, 768}}, {{3072, 768}}, {{768, 3072}}}};
+  ma_muon_tensor t[6];
+  memset(t, 0, sizeof(t));
+  uintptr_t addr = (uintptr_t)1 << 40;
+  for (int i = 0; i < 6; ++i) {{
+    const int64_t n = shapes[i][0] * shapes[i][1];
+    t[i].param = (void*)addr; addr += (uintptr_t)n * 4 + (1 << 20);
+    t[i].grad = (const void*)addr; addr += (uintptr_t)n * 4 + (1 << 20);
+    t[i].momentum = (float*)addr; addr += (uintptr_t)n * 4 + (1 << 20);
+    t[i].batch = 1; t[i].rows = shapes[i][0]; t[i].cols = shapes[i][1]; t[i].views = 1;
+    t[i].param_dtype = MA_F32; t[i].grad_dtype = MA_F32; t[i].lr = 0.02f; t[i].weight_decay = 0.1f;
+  }}
+  ma_muon_hparams hp;
+  memset(&hp, 0, sizeof(hp));
+  hp.beta = 0.95; hp.nesterov = 1; hp.ns_steps = 5; hp.ns_a = 3.4445f; hp.ns_b = -4.7750f; hp.ns_c = 2.0315f;
+  hp.ns_eps = 1e-7f; hp.ns_dtype = MA_BF16; hp.normuon_beta2 = 0.95; hp.muon_plus_eps = 1e-8f;
+  int32_t nm = -1, nb = -1;
+  printf("counts %d", (int)ma_muon_plan_counts(t, 6, &hp, &nm, &nb));
+  printf(" %d %d\\n", nm, nb);
+  printf("workspace %zu\\n", ma_muon_workspace_bytes(t, 6, &hp));
+  ma_matrix_info info;
+  printf("info %d", (int)ma_muon_matrix_info(t, 6, &hp, 4, &info));
+  printf(" %d %d %d %d %d %llu\\n", info.tensor, info.r, info.c, info.rp, info.transposed,
+         (unsigned long long)info.u_offset);
+  /* the status first, then the message: ma_last_error() reads the state the
+     call left behind */
+  t[5].views = 7;                                   /* 7 does not divide 768 */
+  int st = (int)ma_muon_plan_counts(t, 6, &hp, &nm, &nb);
+  printf("views %d %s\\n", st, ma_last_error());
+  t[5].views = 1;
+  t[2].momentum = t[1].momentum;                    /* two tensors sharing momentum */
+  st = (int)muon_step(t, 6, &hp, NULL, 0, NULL);
+  printf("alias %d %s\\n", st, ma_last_error());
+  return 0;
+}}''')
+    exe = tmp_path / "caller"
+    libdir = os.path.dirname(ma.LIB_PATH)
+    subprocess.run(["gcc", "-std=c99", str(src), "-o", str(exe), ma.LIB_PATH, f"-Wl,-rpath,{libdir}"],
+                   check=True)
+    out = subprocess.run([str(exe)], capture_output=True, text=True, check=True).stdout.splitlines()
+    got = {line.split(" ", 1)[0]: line.split(" ", 1)[1] for line in out}
+    wl = workloads.workload(2)
+    specs = wl.muon[:6]
+    arr = (ma.MuonTensorC * 6)()
+    addr = 1 << 40
+    for i, sp in enumerate(specs):
+        n = sp.rows * sp.cols
+        arr[i].param = addr; addr += n * 4 + (1 << 20)
+        arr[i].grad = addr; addr += n * 4 + (1 << 20)
+        arr[i].momentum = addr; addr += n * 4 + (1 << 20)
+        arr[i].batch, arr[i].rows, arr[i].cols, arr[i].views = 1, sp.rows, sp.cols, 1
+        arr[i].param_dtype = arr[i].grad_dtype = ma.MA_F32
+        arr[i].lr, arr[i].weight_decay = 0.02, 0.1
+    hp = ma.muon_hparams(ns_dtype="bf16")
+    _, nm, nb = counts(lib, arr, 6, hp)
+    assert got["counts"] == f"0 {nm} {nb}"
+    assert int(got["workspace"]) == lib.ma_muon_workspace_bytes(arr, 6, ctypes.byref(hp))
+    i4 = info(lib, arr, 6, hp, 4)
+    assert got["info"] == f"0 {i4.tensor} {i4.r} {i4.c} {i4.rp} {i4.transposed} {i4.u_offset}"
+    assert got["views"].startswith("1 ") and "views" in got["views"]
+    assert got["alias"].startswith("3 ") and "overlapping" in got["alias"]
+
+
 # ---------------------------------------------------------------------------
 # descriptors with fake, non-overlapping device addresses
 # ---------------------------------------------------------------------------
