@@ -903,7 +903,8 @@ ma_status ma_muon_queue_info(const ma_muon_tensor* tensors, int32_t n, const ma_
 }
 
 ma_status ma_mfma_bf16_ceiling(float* sink, int32_t blocks, int32_t iters, void* stream) {
-  if (!sink) return fail(MA_E_INVALID, "sink is NULL");
+  if (!sink || reinterpret_cast<uintptr_t>(sink) % alignof(float))
+    return fail(MA_E_INVALID, "sink must be a 4-byte aligned device pointer");
   if (blocks < 1 || blocks > (1 << 20)) return fail(MA_E_INVALID, "blocks must be in [1, 2^20]");
   if (iters < 1 || iters > (1 << 24)) return fail(MA_E_INVALID, "iters must be in [1, 2^24]");
   (void)hipGetLastError();

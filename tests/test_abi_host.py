@@ -829,3 +829,4 @@ def test_mfma_ceiling_validation(lib):
     assert lib.ma_mfma_bf16_ceiling(BASE, 0, 10, None) == 1
     assert lib.ma_mfma_bf16_ceiling(BASE, 4, 0, None) == 1
     assert lib.ma_mfma_bf16_ceiling(BASE, (1 << 20) + 1, 10, None) == 1
+    assert lib.ma_mfma_bf16_ceiling(BASE + 2, 4, 10, None) == 1 and b"aligned" in lib.ma_last_error()
