@@ -13,7 +13,6 @@ persistent launch (ns_persistent_bf16), a launch covers all iterations.
 """
 import argparse
 import json
-import math
 import os
 import sys
 import time
@@ -178,10 +177,8 @@ def cpu_baseline(wl, data, budget_s):
     """The fp64 oracle, untuned, on a bounded sample of the same workload:
     whole Muon updates of the first matrices in tensor order until the time
     budget is spent. Reported in the same unit as the GPU figure."""
-    import numpy as np
     from oracle import muon as omuon
     from workloads import to_numpy
-    from oracle import storage
     try:
         from threadpoolctl import threadpool_info
         pools = [p for p in threadpool_info() if p.get("user_api") == "blas"] or threadpool_info()

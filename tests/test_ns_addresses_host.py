@@ -14,7 +14,6 @@ inside its output buffer, and every output element of the padded matrix must
 be stored exactly once per tile grid (the mirrored tile included). The LDS
 destinations of the loads must fill each stage buffer exactly.
 """
-import math
 
 import numpy as np
 import pytest
