@@ -19,7 +19,7 @@ SOURCES = ["api.hip", "k_momentum.hip", "k_ns_mfma.hip", "k_ns_f32.hip", "k_rowc
            "k_apply.hip", "k_adamw.hip", "k_gradnorm.hip", "k_ceiling.hip"]
 
 ARCH = "gfx950"
-FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wshadow", "-Wno-unused-function",
+FLAGS = [f"--offload-arch={ARCH}", "-O3", "-fPIC", "-std=c++17", "-Wall", "-Wextra", "-Wshadow", "-Wno-unused-function",
          # never emit packed fp32 arithmetic (v_pk_fma_f32 and friends)
          "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
          "-I", INCLUDE, "-I", CSRC]

@@ -68,7 +68,7 @@ __global__ __launch_bounds__(1024) void grad_norm_finalize_kernel(const double* 
   red[threadIdx.x] = s;
   __syncthreads();
   for (int h = 512; h >= 1; h >>= 1) {
-    if (threadIdx.x < h) red[threadIdx.x] += red[threadIdx.x + h];
+    if (static_cast<int>(threadIdx.x) < h) red[threadIdx.x] += red[threadIdx.x + h];
     __syncthreads();
   }
   if (threadIdx.x == 0) {
