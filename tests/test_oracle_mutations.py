@@ -17,13 +17,13 @@ A, B, C = pins.A, pins.B, pins.C
 
 
 def _ns_template(M, steps=5, eps=1e-7, coeffs=(A, B, C), *, wrong_side=False,
-                 spectral=False, drop_eps=False, steps_delta=0):
+                 spectral=False, drop_eps=False, steps_delta=0, norm_power=1):
     X = np.array(M, dtype=np.float64)
     tall = X.shape[0] > X.shape[1]
     if tall:
         X = X.T
     nrm = np.linalg.norm(X, 2) if spectral else np.linalg.norm(X)
-    X = X / (nrm + (0.0 if drop_eps else eps))
+    X = X / (nrm ** norm_power + (0.0 if drop_eps else eps))
     a, b, c = coeffs
     for _ in range(steps + steps_delta):
         Am = X @ X.T
@@ -52,6 +52,11 @@ def ns_four_steps(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale
     return _ns_template(M, steps, eps, coeffs, steps_delta=-1)
 
 
+def ns_norm_squared(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
+    """Normalised by the squared Frobenius norm (the sum of squares, no root)."""
+    return _ns_template(M, steps, eps, coeffs, norm_power=2)
+
+
 def ns_xa_order(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1.0):
     """X (bA + cA^2) instead of (bA + cA^2) X: the operands swap places, which
     only type-checks (and only differs) for a square matrix."""
@@ -68,7 +73,7 @@ def ns_xa_order(M, steps=5, eps=1e-7, coeffs=(A, B, C), table=None, norm_scale=1
     return X.T if tall else X
 
 
-NS_MUTANTS = [ns_flip_b, ns_drop_c, ns_spectral, ns_no_eps, ns_four_steps, ns_xa_order]
+NS_MUTANTS = [ns_flip_b, ns_drop_c, ns_spectral, ns_no_eps, ns_four_steps, ns_xa_order, ns_norm_squared]
 
 
 # a mutant may diverge and overflow; that is part of how it fails
@@ -110,6 +115,11 @@ def decay_dropped(W, U, lr, wd, s):
     return W - lr * s * U
 
 
+def decay_after_update(W, U, lr, wd, s):
+    """The decay factor applied to the already updated weight."""
+    return (1.0 - lr * wd) * (W - lr * s * U)
+
+
 @pytest.mark.parametrize("name,mutant", [
     ("momentum_ema", momentum_no_dampening),
     ("momentum_ema", momentum_swapped),
@@ -118,6 +128,7 @@ def decay_dropped(W, U, lr, wd, s):
     ("shape_scale", scale_no_sqrt),
     ("apply_decoupled", decay_not_lr_scaled),
     ("apply_decoupled", decay_dropped),
+    ("apply_decoupled", decay_after_update),
 ], ids=lambda x: x if isinstance(x, str) else x.__name__)
 def test_step_mutants_caught(name, mutant, monkeypatch):
     monkeypatch.setattr(omuon, name, mutant)
@@ -199,8 +210,15 @@ def normuon_beta_swapped(U, V, beta2):
     return U_hat * (np.linalg.norm(U) / np.linalg.norm(U_hat)), V_new
 
 
+def normuon_no_running_average(U, V, beta2):
+    """V replaced by this step's row means instead of averaged into them."""
+    v_mean = np.mean(U * U, axis=1)
+    U_hat = U * (np.maximum(v_mean, 1e-30) ** -0.5)[:, None]
+    return U_hat * (np.linalg.norm(U) / np.linalg.norm(U_hat)), v_mean
+
+
 @pytest.mark.parametrize("mutant", [normuon_column_axis, normuon_not_norm_preserving,
-                                    normuon_beta_swapped], ids=lambda f: f.__name__)
+                                    normuon_beta_swapped, normuon_no_running_average], ids=lambda f: f.__name__)
 def test_normuon_mutants_caught(mutant):
     with pytest.raises((AssertionError, ValueError)):
         pins.check_normuon(mutant)
@@ -216,7 +234,14 @@ def muon_plus_eps_outside(U, eps):
     return U / (np.sqrt(np.sum(U * U, axis=0, keepdims=True)) + eps)
 
 
-@pytest.mark.parametrize("mutant", [muon_plus_columns_first, muon_plus_eps_outside],
+def muon_plus_unit_rms(U, eps):
+    """Rows, then columns, scaled to unit RMS instead of unit L2 norm."""
+    U = U / np.sqrt(np.mean(U * U, axis=1, keepdims=True) + eps)
+    U = U / np.sqrt(np.mean(U * U, axis=0, keepdims=True) + eps)
+    return U
+
+
+@pytest.mark.parametrize("mutant", [muon_plus_columns_first, muon_plus_eps_outside, muon_plus_unit_rms],
                          ids=lambda f: f.__name__)
 def test_muon_plus_mutants_caught(mutant):
     with pytest.raises(AssertionError):
@@ -270,8 +295,24 @@ def adamw_coupled_decay(p, g, m, v, lr, wd, b1, b2, eps, step):
     return p - lr * mh / (np.sqrt(vh) + eps), m, v
 
 
-@pytest.mark.parametrize("mutant", [adamw_eps_inside, adamw_no_bias_correction,
-                                    adamw_coupled_decay], ids=lambda f: f.__name__)
+def adamw_bias_next_step(p, g, m, v, lr, wd, b1, b2, eps, step):
+    """Bias correction with the next step's count."""
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh, vh = m / (1 - b1 ** (step + 1)), v / (1 - b2 ** (step + 1))
+    return p - lr * (mh / (np.sqrt(vh) + eps) + wd * p), m, v
+
+
+def adamw_decay_not_lr_scaled(p, g, m, v, lr, wd, b1, b2, eps, step):
+    m = b1 * m + (1 - b1) * g
+    v = b2 * v + (1 - b2) * g * g
+    mh, vh = m / (1 - b1 ** step), v / (1 - b2 ** step)
+    return p - lr * mh / (np.sqrt(vh) + eps) - wd * p, m, v
+
+
+@pytest.mark.parametrize("mutant", [adamw_eps_inside, adamw_no_bias_correction, adamw_coupled_decay,
+                                    adamw_bias_next_step, adamw_decay_not_lr_scaled],
+                         ids=lambda f: f.__name__)
 def test_adamw_mutants_caught(mutant):
     with pytest.raises(AssertionError):
         pins.check_adamw(mutant)
