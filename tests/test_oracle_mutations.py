@@ -5,6 +5,8 @@ Each mutant replaces one oracle function with a copy carrying a single slip
 comparison). The pins in ``test_oracle_pins.py`` must reject every mutant;
 that is what makes them pins rather than retypings of the oracle.
 """
+import math
+
 import numpy as np
 import pytest
 
@@ -403,6 +405,32 @@ def test_cautious_adamw_mutants_caught(mutant, monkeypatch):
 def test_grad_norm_without_sqrt_caught(monkeypatch):
     orig = ognorm.global_norm
     monkeypatch.setattr(ognorm, "global_norm", lambda grads: orig(grads) ** 2)
+    with pytest.raises(AssertionError):
+        pins.test_global_norm_and_clip_closed_forms()
+
+
+def _clip_always(norm, max_norm):
+    """Rescales to max_norm also when the norm is below it."""
+    finite = math.isfinite(norm)
+    return (max_norm / norm if (finite and max_norm > 0) else 1.0), not finite
+
+
+def _clip_skip_when_large(norm, max_norm):
+    """Skips the step when the norm exceeds max_norm instead of when it is not finite."""
+    finite = math.isfinite(norm)
+    big = max_norm > 0 and norm > max_norm
+    return (max_norm / norm if (finite and big) else 1.0), (not finite) or big
+
+
+def _clip_with_eps(norm, max_norm):
+    """max_norm / (norm + 1e-6), the form some libraries use."""
+    finite = math.isfinite(norm)
+    return (max_norm / (norm + 1e-6) if (finite and max_norm > 0 and norm > max_norm) else 1.0), not finite
+
+
+@pytest.mark.parametrize("mutant", [_clip_always, _clip_skip_when_large, _clip_with_eps], ids=lambda f: f.__name__)
+def test_clip_mutants_caught(mutant, monkeypatch):
+    monkeypatch.setattr(ognorm, "clip_state", mutant)
     with pytest.raises(AssertionError):
         pins.test_global_norm_and_clip_closed_forms()
 
