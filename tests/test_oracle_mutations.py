@@ -528,3 +528,22 @@ def test_normuon_composition_mutants_caught(mutant, monkeypatch):
     monkeypatch.setattr(omuon, "matrix_update", mutant)
     with pytest.raises(AssertionError):
         pins.check_normuon_wdmask_two_steps()
+
+
+# -- bf16 moments: the stochastic-rounding key -----------------------------------
+def _key_without_tensor(seed, step, leaf, moment):
+    return _REAL_KEY(seed, step, 0, moment)
+
+
+def _key_without_step(seed, step, leaf, moment):
+    return _REAL_KEY(seed, 0, leaf, moment)
+
+
+_REAL_KEY = ostorage.sr_key
+
+
+@pytest.mark.parametrize("mutant", [_key_without_tensor, _key_without_step], ids=lambda f: f.__name__)
+def test_rounding_key_mutants_caught(mutant, monkeypatch):
+    monkeypatch.setattr(ostorage, "sr_key", mutant)
+    with pytest.raises(AssertionError):
+        pins.test_adamw_bf16_moments_use_the_step_tensor_and_moment_keys()

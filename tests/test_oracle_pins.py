@@ -687,9 +687,13 @@ def test_adamw_bf16_moments_use_the_step_tensor_and_moment_keys():
                  "m": storage.round_bf16_bits(rng.normal(0, 1e-4, n)),
                  "v": storage.round_bf16_bits(rng.uniform(1e-8, 1e-6, n)), "moment_dtype": "bf16",
                  "lr": 1e-3, "wd": 0.1}
-    ts = [t(), t()]
+    t0 = t()
+    ts = [t0, {k: (v.copy() if isinstance(v, np.ndarray) else v) for k, v in t0.items()}]   # identical inputs
     hp = {"beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "step": 3, "seed": 42}
     out = oadamw.adamw_step(ts, hp)
+    # the same values in two tensors draw different noise (the tensor index is in the key)
+    assert np.array_equal(out[0]["param"], out[1]["param"])
+    assert not np.array_equal(out[0]["m"], out[1]["m"]) and not np.array_equal(out[0]["v"], out[1]["v"])
     for k, (ti, o) in enumerate(zip(ts, out)):
         p64, m64, v64 = oadamw.adamw_update(storage.decode(ti["param"], "f32"), storage.decode(ti["grad"], "f32"),
                                             storage.decode(ti["m"], "bf16"), storage.decode(ti["v"], "bf16"),
