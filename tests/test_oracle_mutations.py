@@ -185,6 +185,32 @@ def whole_parent_ns(W, G, Bm, V, views, hp, lr, wd):
     return omuon.muon_tensor_step(W, G, Bm, V, 1, hp, lr, wd)
 
 
+def batch_norm_shared(W, G, Bm, V, views, hp, lr, wd):
+    """Every batch entry normalised by the Frobenius norm of the whole batch
+    before its own iteration, instead of by its own norm."""
+    beta = hp.get("beta", 0.95)
+    B_new = omuon.momentum_ema(Bm, G, beta)
+    Q = omuon.nesterov_lerp(G, B_new, beta)
+    batch, rows, cols = W.shape
+    total = np.linalg.norm(Q)
+    Wn = np.empty_like(W)
+    for b in range(batch):
+        X = Q[b].T if rows > cols else Q[b]
+        X = X / (total + 1e-7)
+        for _ in range(5):
+            Am = X @ X.T
+            X = A * X + (B * Am + C * (Am @ Am)) @ X
+        U = X.T if rows > cols else X
+        Wn[b] = omuon.apply_decoupled(W[b], U, lr, wd, omuon.shape_scale(rows, cols))
+    return Wn, B_new, None, None
+
+
+def test_batch_norm_shared_caught(monkeypatch):
+    monkeypatch.setattr(omuon, "muon_tensor_step", batch_norm_shared)
+    with pytest.raises(AssertionError):
+        pins.test_batch_entries_are_independent()
+
+
 @pytest.mark.parametrize("mutant", [view_scale_from_parent, whole_parent_ns],
                          ids=lambda f: f.__name__)
 def test_view_mutants_caught(mutant):
