@@ -99,6 +99,40 @@ def test_ns_scalar_constants():
     assert np.abs(omuon.newton_schulz(Q) - f * Q).max() < 1e-13
 
 
+def check_ns_equivariance(ns=None, trials=60):
+    """NS(P X Q) = P NS(X) Q for orthogonal P and Q: the iteration is a
+    polynomial in X X^T applied to X, so it commutes with rotations on both
+    sides (the Frobenius norm is rotation-invariant too). Random shapes from
+    1 x 1 to 12 x 12, square, wide and tall."""
+    ns = ns or omuon.newton_schulz
+    r = rng(41)
+    for _ in range(trials):
+        m, n = int(r.integers(1, 13)), int(r.integers(1, 13))
+        X = r.standard_normal((m, n))
+        P, _ = np.linalg.qr(r.standard_normal((m, m)))
+        Q, _ = np.linalg.qr(r.standard_normal((n, n)))
+        want = P @ ns(X) @ Q
+        got = ns(P @ X @ Q)
+        assert np.abs(got - want).max() < 1e-12 * max(1.0, np.abs(want).max()), (m, n)
+
+
+def test_ns_orthogonal_equivariance():
+    check_ns_equivariance()
+
+
+def test_ns_scale_invariance():
+    """NS(c X) = NS(X) up to the eps term: with ||X||_F ~ 10 and c from 1e-2 to
+    1e6, the normalised inputs differ by at most eps / (c ||X||) relative."""
+    r = rng(42)
+    for shape in [(5, 3), (3, 5), (6, 6), (1, 7)]:
+        X = r.standard_normal(shape) * 4
+        base = omuon.newton_schulz(X * 1e6)        # eps negligible
+        for c in [1e-2, 1.0, 1e3]:
+            got = omuon.newton_schulz(X * c)
+            bound = 50 * EPS / (c * np.linalg.norm(X))   # the eps term, amplified by at most ~phi'(x)^5
+            assert np.abs(got - base).max() <= bound + 1e-13, (shape, c)
+
+
 def test_ns_transpose_symmetry():
     r = rng(5)
     for shape in [(7, 3), (3, 7), (16, 48)]:
