@@ -573,3 +573,28 @@ def test_rounding_key_mutants_caught(mutant, monkeypatch):
     monkeypatch.setattr(ostorage, "sr_key", mutant)
     with pytest.raises(AssertionError):
         pins.test_adamw_bf16_moments_use_the_step_tensor_and_moment_keys()
+
+
+# -- the library pins (torch.optim.Muon, torch.optim.AdamW in float64) catch the
+# -- same slips on their own ---------------------------------------------------
+STEP_MUTANTS = [("momentum_ema", momentum_no_dampening), ("momentum_ema", momentum_swapped),
+                ("nesterov_lerp", nesterov_old_sign), ("shape_scale", scale_swapped),
+                ("shape_scale", scale_no_sqrt), ("apply_decoupled", decay_not_lr_scaled),
+                ("apply_decoupled", decay_dropped), ("apply_decoupled", decay_after_update)]
+
+
+@pytest.mark.parametrize("name,mutant", STEP_MUTANTS, ids=lambda x: x if isinstance(x, str) else x.__name__)
+def test_torch_muon_pin_catches_step_mutants(name, mutant, monkeypatch):
+    monkeypatch.setattr(omuon, name, mutant)
+    with pytest.raises(AssertionError):
+        pins.test_muon_steps_match_torch_optim_muon()
+
+
+@pytest.mark.parametrize("mutant", [adamw_eps_inside, adamw_no_bias_correction, adamw_coupled_decay,
+                                    adamw_bias_next_step, adamw_decay_not_lr_scaled], ids=lambda f: f.__name__)
+def test_torch_adamw_pin_catches_adamw_mutants(mutant, monkeypatch):
+    def wrapped(p, g, m, v, lr, wd, b1, b2, eps, step, cautious=False):
+        return mutant(p, g, m, v, lr, wd, b1, b2, eps, step)
+    monkeypatch.setattr(oadamw, "adamw_update", wrapped)
+    with pytest.raises(AssertionError):
+        pins.test_adamw_matches_torch_optim_adamw()
