@@ -93,7 +93,12 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
         return _lib
     if not os.path.exists(path):
         raise ImportError(f"{path} is missing: build it with `python -m muon_adamw_amd.build`")
-    lib = ctypes.CDLL(path)
+    _lib = declare(ctypes.CDLL(path))
+    return _lib
+
+
+def declare(lib: ctypes.CDLL) -> ctypes.CDLL:
+    """Sets the argument and result types of every function the header declares."""
     P, I32, I64, SZ = ctypes.c_void_p, ctypes.c_int32, ctypes.c_int64, ctypes.c_size_t
     lib.muon_step.argtypes = [ctypes.POINTER(MuonTensorC), I32, ctypes.POINTER(MuonHParamsC), P, SZ, P]
     lib.muon_step.restype = ctypes.c_int
@@ -128,7 +133,6 @@ def load_library(path: str = LIB_PATH) -> ctypes.CDLL:
     lib.ma_muon_queue_info.restype = ctypes.c_int
     lib.ma_mfma_bf16_ceiling.argtypes = [P, I32, I32, P]
     lib.ma_mfma_bf16_ceiling.restype = ctypes.c_int
-    _lib = lib
     return lib
 
 
