@@ -35,6 +35,8 @@ def load(path: str = LIB) -> ctypes.CDLL:
     lib.hipsim_set_workers.restype = ctypes.c_int
     lib.hipsim_set_dma_deferred.argtypes = [ctypes.c_int]
     lib.hipsim_set_dma_deferred.restype = ctypes.c_int
+    lib.hipsim_set_xcds.argtypes = [ctypes.c_int]
+    lib.hipsim_set_xcds.restype = ctypes.c_int
     lib.hipsim_set_schedule.argtypes = [ctypes.c_int]
     lib.hipsim_set_schedule.restype = ctypes.c_int
     lib.hipsim_fault.argtypes = []

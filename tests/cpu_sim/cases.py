@@ -193,7 +193,7 @@ def case_adamw(sim):
 # ---------------------------------------------------------------------------
 # Newton-Schulz alone
 # ---------------------------------------------------------------------------
-def newton_schulz(sim, x_stored, dt, hp=None):
+def newton_schulz(sim, x_stored, dt, hp=None, want_status=0):
     lib = sim.lib
     shape = x_stored.shape
     batch, rows, cols = (1, *shape) if len(shape) == 2 else shape
@@ -207,7 +207,7 @@ def newton_schulz(sim, x_stored, dt, hp=None):
                                 cpu_sim.addr(ws), need, None), f"newton-schulz {shape} {dt}")
     st = ctypes.c_int32(-1)
     sim.ok(lib.ma_muon_step_status(cpu_sim.addr(ws), ctypes.byref(st), None), "status")
-    assert st.value == 0, ("status word", st.value)
+    assert st.value == want_status, ("status word", st.value, want_status)
     return out
 
 
@@ -236,6 +236,56 @@ def case_ns_schedules(sim):
         finally:
             del os.environ["MA_NS_SCHEDULE"]
         assert np.array_equal(a, b), (shape, int(np.sum(a != b)))
+
+
+def case_ns_layouts(sim):
+    """SQUARE and APPLY read their operands k-major (at most 2048 padded rows)
+    or row-wise (larger matrices): forced each way, the same bits, and the
+    row-wise results within the oracle's bar."""
+    for k, shape in enumerate([(300, 700), (640, 256), (2, 260, 130)]):
+        x = storage.round_bf16_bits(randn(shape, 600 + k))
+        outs = []
+        for layout in ("rows", "kmajor"):
+            os.environ["MA_NS_OPERANDS"] = layout
+            try:
+                outs.append(newton_schulz(sim, x, "bf16").copy())
+            finally:
+                del os.environ["MA_NS_OPERANDS"]
+        assert np.array_equal(outs[0], outs[1]), (shape, int(np.sum(outs[0] != outs[1])))
+        xs = x if x.ndim == 3 else x[None]
+        got = outs[0] if x.ndim == 3 else outs[0][None]
+        for b in range(xs.shape[0]):
+            check_local(dec(got[b], "bf16"), omuon.newton_schulz(dec(xs[b], "bf16")), 2e-2, (shape, b))
+
+
+def case_status_undrained(sim):
+    """Workgroups reach only four of the eight XCD queues (a device where some
+    XCD gets none): the persistent launch finishes and its status word says
+    a queue was left (NS_QUEUE_UNDRAINED); with all eight, 0 and the
+    oracle's result."""
+    x = storage.round_bf16_bits(randn((16, 128, 256), 700))
+    sim.lib.hipsim_set_xcds(4)
+    try:
+        newton_schulz(sim, x, "bf16", want_status=ma.NS_QUEUE_UNDRAINED)
+    finally:
+        sim.lib.hipsim_set_xcds(8)
+    out = newton_schulz(sim, x, "bf16")
+    for b in range(0, 16, 5):
+        check_local(dec(out[b], "bf16"), omuon.newton_schulz(dec(x[b], "bf16")), 2e-2, b)
+
+
+def case_mfma_ceiling(sim):
+    """The matrix-core ceiling loop: each block's sink value is eight times
+    the sum of lane 0's sixteen accumulators after `iters` products of the
+    kernel's fixed operands (exact in fp32)."""
+    blocks, iters = 3, 5
+    sink = sim.arena.array((blocks,), np.float32)
+    sim.ok(sim.lib.ma_mfma_bf16_ceiling(cpu_sim.addr(sink), blocks, iters, None), "ceiling")
+    A = np.array([[0.125 * (((32 * (k // 8) + i) + k % 8) & 7) for k in range(16)] for i in range(32)])
+    B = np.array([[0.0625 * (((32 * (k // 8) + c) + 3 * (k % 8)) & 15) for c in range(32)] for k in range(16)])
+    rows = [8 * (r // 4) + r % 4 for r in range(16)]
+    want = 8 * iters * (A @ B)[rows, 0].sum()
+    assert np.all(sink == np.float32(want)), (sink, want)
 
 
 # ---------------------------------------------------------------------------

@@ -84,6 +84,10 @@ std::atomic<bool> g_defer_dma{true};
 // can go before a block barrier, in ascending / descending wave order (the
 // waves drift apart as far as the barriers allow)
 std::atomic<int> g_schedule{0};
+// XCDs that receive workgroups: the dispatcher hands workgroup b to XCD
+// b mod this (8 on an MI355X; fewer stands for a device where some XCD gets
+// no workgroup, which the persistent launch must report)
+std::atomic<int> g_xcds{8};
 std::atomic<long long> g_launches{0}, g_blocks{0}, g_wave_ops{0}, g_barriers{0}, g_dma{0}, g_mfma{0},
     g_skipped{0};
 thread_local hipError_t t_last = hipSuccess;
@@ -469,8 +473,7 @@ int mov_dpp(int v, int ctrl, int row_mask, int bank_mask, bool, int site) {
 uint32_t getreg(int imm) {
   const int id = imm & 63, off = (imm >> 6) & 31, size = ((imm >> 11) & 31) + 1;
   if (id != 20) fault("s_getreg of hardware register %d is not simulated", id);
-  // the dispatcher hands workgroup b to XCD b mod 8
-  const uint32_t v = t_lane->blk->bid.x % 8;
+  const uint32_t v = t_lane->blk->bid.x % static_cast<uint32_t>(g_xcds.load());
   return (v >> off) & (size >= 32 ? ~0u : ((1u << size) - 1));
 }
 
@@ -576,6 +579,7 @@ int hipsim_set_workers(int n) {
   return old;
 }
 int hipsim_set_dma_deferred(int on) { return hipsim::g_defer_dma.exchange(on != 0) ? 1 : 0; }
+int hipsim_set_xcds(int n) { return hipsim::g_xcds.exchange(n < 1 || n > 8 ? 8 : n); }
 int hipsim_set_schedule(int policy) { return hipsim::g_schedule.exchange(policy < 0 || policy > 2 ? 0 : policy); }
 const char* hipsim_fault() { return hipsim::g_fault.c_str(); }
 void hipsim_clear_fault() {

@@ -15,7 +15,10 @@ Then the parity cases of ``cases.py`` run the library through its C entry
 points, each in a child process, compared with the oracle at the GPU tests'
 bars:
 - the global norm (also at 1e20) and AdamW (bf16 moments too);
-- fp32 and bf16 Newton-Schulz alone, and both bf16 schedules bit for bit;
+- fp32 and bf16 Newton-Schulz alone; both bf16 schedules, and both operand
+  layouts, bit for bit;
+- the status word when some XCD's queue gets no workgroup;
+- the matrix-core ceiling loop against its closed form;
 - whole Muon steps with every epilogue.
 The cases run under the three lane schedules and with guard pages before
 and after the buffers.
@@ -159,6 +162,7 @@ CASES = [
     ("grad_norm", ()), ("adamw", ("--mode", "head")),
     ("ns_f32", ()), ("ns_bf16", ()), ("ns_bf16", ("--schedule", "waves-up")),
     ("ns_bf16", ("--schedule", "waves-down", "--mode", "head")), ("ns_schedules", ("--schedule", "waves-down")),
+    ("ns_layouts", ("--schedule", "waves-up")), ("status_undrained", ()), ("mfma_ceiling", ()),
     ("single_256x128", ()), ("muon_f32", ("--mode", "head")), ("muon_f32", ("--schedule", "waves-up")),
     ("muon_bf16", ()), ("muon_bf16", ("--schedule", "waves-down", "--mode", "head")),
 ]
