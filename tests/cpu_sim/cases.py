@@ -291,10 +291,10 @@ def case_mfma_ceiling(sim):
 # ---------------------------------------------------------------------------
 # whole Muon steps
 # ---------------------------------------------------------------------------
-def muon_step(sim, wl, tol_ns, update_tol=None):
+def muon_step(sim, wl, tol_ns, update_tol=None, only=None):
     lib = sim.lib
     h = hp_dict(wl.muon_hp)
-    data = workloads.generate(wl, device="cpu")
+    data = workloads.generate(wl, device="cpu", gen_device="cpu", only=only)
     tens = [t for t in data.muon if t is not None]
     arr = (ma.MuonTensorC * len(tens))()
     bufs = []
@@ -379,6 +379,50 @@ def case_muon_f32(sim):
 def case_muon_bf16(sim):
     for v in VARIANTS[:4]:
         muon_step(sim, aspect2_workload("epilogue_bf16", 42, ns_dtype="bf16", **dict(v)), 2e-2)
+
+
+def case_gpt_layer0(sim):
+    """Layer 0 of the GPT 12L d768 workload at its real shapes (q, k, v, o
+    768 x 768, up 3072 x 768 tall, down 768 x 3072): multi-tile matrices,
+    fp32 storage, bf16 Newton-Schulz."""
+    muon_step(sim, workloads.workload(2), 2e-2, only=range(6))
+
+
+def minis():
+    """Each larger workload's structure and hyperparameters at a size the
+    simulator runs in seconds."""
+    S = workloads.MuonTensorSpec
+    bf = dict(param_dtype="bf16", grad_dtype="bf16")
+    # k keeps 512 rows: with 1% of the gradient x100, a bf16 chain over 128-256
+    # rows already puts single columns near the column bar (the workload's k
+    # has 1024 rows, where the bars were calibrated)
+    llama = workloads.Workload("llama_mini", 12, (
+        S("q", 1, 512, 512, **bf, outlier_frac=0.01, outlier_scale=100.0),
+        S("k", 1, 512, 1536, **bf, outlier_frac=0.01, outlier_scale=100.0),
+        S("gate_up", 1, 2 * 896, 512, views=2, **bf, outlier_frac=0.01, outlier_scale=100.0),
+        S("down", 1, 512, 896, **bf, outlier_frac=0.01, outlier_scale=100.0)),
+        (), workloads.MuonHParams(ns_dtype="bf16"))
+    moe = workloads.Workload("moe_mini", 13, (
+        S("experts.gate_up", 4, 2 * 352, 512, views=2), S("experts.down", 4, 512, 352)),
+        (), workloads.MuonHParams(ns_dtype="bf16", normuon=True, normuon_beta2=0.95, cautious="wd_mask"))
+    wide = workloads.Workload("wide_mini", 14, (
+        S("q", 1, 512, 512, **bf, param_std=0.01, grad_std=1e-4),
+        S("up", 1, 1792, 512, **bf, param_std=0.01, grad_std=1e-4),
+        S("down", 1, 512, 1792, **bf, param_std=0.01, grad_std=1e-4)),
+        (), workloads.MuonHParams(ns_dtype="bf16", muon_plus=True, muon_plus_eps=1e-8, cautious="wrapper"))
+    return {"llama": llama, "moe": moe, "wide": wide}
+
+
+def case_llama_mini(sim):
+    muon_step(sim, minis()["llama"], 2e-2)
+
+
+def case_moe_mini(sim):
+    muon_step(sim, minis()["moe"], 2e-2)
+
+
+def case_wide_mini(sim):
+    muon_step(sim, minis()["wide"], 2e-2)
 
 
 def case_single_256x128(sim):

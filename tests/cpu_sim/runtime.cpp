@@ -4,7 +4,6 @@
 #include <hip/hip_runtime.h>
 
 #include <sys/mman.h>
-#include <ucontext.h>
 #include <unistd.h>
 
 #include <atomic>
@@ -25,6 +24,60 @@ thread_local Lane* t_lane = nullptr;
 
 namespace {
 
+// Fiber switch for x86-64 (System V): saves the callee-saved registers on
+// the current stack, stores the stack pointer to *save, continues on `next`
+// (a stack saved the same way, or one prepared by fiber_stack). No system
+// call, unlike swapcontext. The floating-point control state (MXCSR, x87
+// control word) is the thread's and is not switched: no kernel changes it.
+extern "C" void hipsim_switch(void** save, void* next);
+extern "C" void hipsim_fiber_start();
+asm(R"(
+  .text
+  .globl hipsim_switch
+  .type hipsim_switch, @function
+hipsim_switch:
+  pushq %rbp
+  pushq %rbx
+  pushq %r12
+  pushq %r13
+  pushq %r14
+  pushq %r15
+  movq %rsp, (%rdi)
+  movq %rsi, %rsp
+  popq %r15
+  popq %r14
+  popq %r13
+  popq %r12
+  popq %rbx
+  popq %rbp
+  ret
+  .size hipsim_switch, .-hipsim_switch
+
+  .globl hipsim_fiber_start
+  .type hipsim_fiber_start, @function
+hipsim_fiber_start:
+  andq $-16, %rsp
+  call *%r12
+  ud2
+  .size hipsim_fiber_start, .-hipsim_fiber_start
+)");
+
+// A fresh fiber on the stack [lo, lo + size): the first switch to the
+// returned pointer enters fn() through hipsim_fiber_start.
+void* fiber_stack(char* lo, size_t size, void (*fn)()) {
+  uint64_t* top = reinterpret_cast<uint64_t*>(reinterpret_cast<uintptr_t>(lo + size) & ~uintptr_t(15));
+  uint64_t* sp = top - 8;
+  sp[0] = 0;                                     // r15
+  sp[1] = 0;                                     // r14
+  sp[2] = 0;                                     // r13
+  sp[3] = reinterpret_cast<uint64_t>(fn);        // r12: the fiber's function
+  sp[4] = 0;                                     // rbx
+  sp[5] = 0;                                     // rbp
+  sp[6] = reinterpret_cast<uint64_t>(&hipsim_fiber_start);   // return address
+  sp[7] = 0;
+  return sp;
+}
+
 enum State { RUNNABLE, AT_WAVE, AT_BAR, SLEEPING, EXITED };
 
 struct Pending {
@@ -33,7 +86,7 @@ struct Pending {
 };
 
 struct LaneImpl {
-  ucontext_t ctx;
+  void* sp = nullptr;     // saved stack pointer of the suspended fiber
   State st = EXITED;
   int site = 0;
   Resolver res = nullptr;
@@ -47,7 +100,7 @@ struct SimFault {};
 
 // One OS thread that runs blocks: the lanes of its current block are fibers.
 struct Worker {
-  ucontext_t sched;
+  void* sched = nullptr;  // saved stack pointer of the scheduler
   Block blk;
   Lane lanes[kMaxLanes];
   LaneImpl impl[kMaxLanes];
@@ -108,7 +161,7 @@ LaneImpl& cur_impl() {
 void yield_to_sched() {
   Worker& W = *t_worker;
   LaneImpl& I = W.impl[t_lane - W.lanes];
-  swapcontext(&I.ctx, &W.sched);
+  hipsim_switch(&I.sp, W.sched);
 }
 
 void complete_dma(LaneImpl& I, size_t keep) {
@@ -125,7 +178,7 @@ void fiber_entry() {
   LaneImpl& I = cur_impl();
   complete_dma(I, 0);
   I.st = EXITED;
-  swapcontext(&I.ctx, &W.sched);
+  hipsim_switch(&I.sp, W.sched);
   abort();  // an exited lane is never resumed
 }
 
@@ -156,11 +209,7 @@ bool run_block(Worker& W, unsigned b, dim3 grid, dim3 block) {
     LaneImpl& I = W.impl[l];
     I.st = RUNNABLE;
     I.dma.clear();
-    getcontext(&I.ctx);
-    I.ctx.uc_stack.ss_sp = W.stack_of(l);
-    I.ctx.uc_stack.ss_size = kStack;
-    I.ctx.uc_link = nullptr;
-    makecontext(&I.ctx, fiber_entry, 0);
+    I.sp = fiber_stack(W.stack_of(l), kStack, fiber_entry);
   }
   const int nwaves = (n + 63) / 64;
   const int policy = g_schedule.load();
@@ -219,7 +268,7 @@ bool run_block(Worker& W, unsigned b, dim3 grid, dim3 block) {
         I.st = RUNNABLE;
         t_lane = &W.lanes[l];
         t_in_lane = true;
-        swapcontext(&W.sched, &I.ctx);
+        hipsim_switch(&W.sched, I.sp);
         t_in_lane = false;
         ran = true;
         if (W.impl[l].st == SLEEPING) slept = true;
@@ -358,25 +407,31 @@ void resolve_mfma(Lane* const* lanes, const unsigned char* act) {
   for (int l = 0; l < 64; ++l)
     if (!act[l]) fault("v_mfma_f32_32x32x16_bf16 with inactive lane %d", l);
   g_mfma.fetch_add(1, std::memory_order_relaxed);
-  float A[32][16], B[16][32];
+  // A row i and B column j both come from lanes i (or j) and 32 + i
+  // (bf16 bits are the top half of the fp32 pattern)
+  double A[32][16], B[16][32];
   for (int l = 0; l < 64; ++l) {
-    bf16x8_t a, b;
-    memcpy(&a, lanes[l]->xin, 16);
-    memcpy(&b, lanes[l]->xin + 16, 16);
+    uint16_t a[8], b[8];
+    memcpy(a, lanes[l]->xin, 16);
+    memcpy(b, lanes[l]->xin + 16, 16);
     for (int j = 0; j < 8; ++j) {
-      A[l % 32][8 * (l / 32) + j] = static_cast<float>(a[j]);
-      B[8 * (l / 32) + j][l % 32] = static_cast<float>(b[j]);
+      A[l % 32][8 * (l / 32) + j] = static_cast<double>(__builtin_bit_cast(float, uint32_t(a[j]) << 16));
+      B[8 * (l / 32) + j][l % 32] = static_cast<double>(__builtin_bit_cast(float, uint32_t(b[j]) << 16));
     }
   }
+  // Products of bf16 values are exact in double and their 16-term sums
+  // nearly so. D = C + AB is rounded to fp32 once. Each output sums its
+  // terms in k order; the inner loop runs over outputs, so it vectorises.
+  double P[32][32] = {};
+  for (int i = 0; i < 32; ++i)
+    for (int k = 0; k < 16; ++k) {
+      const double a = A[i][k];
+      for (int j = 0; j < 32; ++j) P[i][j] += a * B[k][j];
+    }
   for (int l = 0; l < 64; ++l) {
     f32x16_t c, d;
     memcpy(&c, lanes[l]->xin + 32, 64);
-    for (int r = 0; r < 16; ++r) {
-      const int row = 8 * (r / 4) + 4 * (l / 32) + r % 4, col = l % 32;
-      double s = c[r];
-      for (int k = 0; k < 16; ++k) s += static_cast<double>(A[row][k]) * B[k][col];
-      d[r] = static_cast<float>(s);
-    }
+    for (int r = 0; r < 16; ++r) d[r] = static_cast<float>(c[r] + P[8 * (r / 4) + 4 * (l / 32) + r % 4][l % 32]);
     memcpy(lanes[l]->xout, &d, 64);
   }
 }

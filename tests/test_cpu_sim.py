@@ -19,7 +19,10 @@ bars:
   layouts, bit for bit;
 - the status word when some XCD's queue gets no workgroup;
 - the matrix-core ceiling loop against its closed form;
-- whole Muon steps with every epilogue.
+- whole Muon steps with every epilogue;
+- layer 0 of the GPT workload at its real shapes, and small copies of the
+  Llama, MoE and wide workloads (their dtypes, views, batches, outliers and
+  epilogues).
 The cases run under the three lane schedules and with guard pages before
 and after the buffers.
 
@@ -165,6 +168,8 @@ CASES = [
     ("ns_layouts", ("--schedule", "waves-up")), ("status_undrained", ()), ("mfma_ceiling", ()),
     ("single_256x128", ()), ("muon_f32", ("--mode", "head")), ("muon_f32", ("--schedule", "waves-up")),
     ("muon_bf16", ()), ("muon_bf16", ("--schedule", "waves-down", "--mode", "head")),
+    ("gpt_layer0", ()), ("llama_mini", ("--schedule", "waves-up")), ("moe_mini", ("--mode", "head")),
+    ("wide_mini", ("--schedule", "waves-down")),
 ]
 
 
@@ -179,7 +184,8 @@ def case_results():
     current; each test waits for its own."""
     simbuild.build()
     ex = ThreadPoolExecutor(4)
-    futs = {(c, a): ex.submit(_run, c, a) for c, a in CASES}
+    slow_first = sorted(CASES, key=lambda ca: ca[0] not in ("wide_mini", "gpt_layer0", "ns_layouts", "ns_schedules"))
+    futs = {(c, a): ex.submit(_run, c, a) for c, a in slow_first}
     yield futs
     ex.shutdown(wait=True)
 
