@@ -291,11 +291,8 @@ def case_mfma_ceiling(sim):
 # ---------------------------------------------------------------------------
 # whole Muon steps
 # ---------------------------------------------------------------------------
-def muon_step(sim, wl, tol_ns, update_tol=None, only=None):
-    lib = sim.lib
-    h = hp_dict(wl.muon_hp)
-    data = workloads.generate(wl, device="cpu", gen_device="cpu", only=only)
-    tens = [t for t in data.muon if t is not None]
+def load_muon(sim, tens):
+    """Guarded copies of the tensors' buffers and their C descriptors."""
     arr = (ma.MuonTensorC * len(tens))()
     bufs = []
     for i, t in enumerate(tens):
@@ -311,21 +308,41 @@ def muon_step(sim, wl, tol_ns, update_tol=None, only=None):
         d.batch, d.rows, d.cols, d.views = t.spec.batch, t.spec.rows, t.spec.cols, t.spec.views
         d.param_dtype, d.grad_dtype = DT[t.spec.param_dtype], DT[t.spec.grad_dtype]
         d.lr, d.weight_decay = t.spec.lr, t.spec.wd
-    hp = hp_c(wl.muon_hp)
+    return arr, bufs
+
+
+def run_muon(sim, arr, n, hp, what="muon_step"):
+    """One muon_step on the descriptors; returns (matrix infos, workspace)."""
+    lib = sim.lib
     nm, nb = ctypes.c_int32(0), ctypes.c_int32(0)
-    sim.ok(lib.ma_muon_plan_counts(arr, len(tens), ctypes.byref(hp), ctypes.byref(nm), ctypes.byref(nb)), "plan")
+    sim.ok(lib.ma_muon_plan_counts(arr, n, ctypes.byref(hp), ctypes.byref(nm), ctypes.byref(nb)), "plan")
     infos = []
     for k in range(nm.value):
         info = ma.MatrixInfoC()
-        sim.ok(lib.ma_muon_matrix_info(arr, len(tens), ctypes.byref(hp), k, ctypes.byref(info)), "info")
+        sim.ok(lib.ma_muon_matrix_info(arr, n, ctypes.byref(hp), k, ctypes.byref(info)), "info")
         infos.append({f: getattr(info, f) for f, _ in ma.MatrixInfoC._fields_ if f != "pad_"})
-    before = [(P.copy(), M.copy(), None if V is None else V.copy()) for P, _, M, V in bufs]
-    need = lib.ma_muon_workspace_bytes(arr, len(tens), ctypes.byref(hp))
+    need = lib.ma_muon_workspace_bytes(arr, n, ctypes.byref(hp))
     ws = sim.arena.bytes(need)
-    sim.ok(lib.muon_step(arr, len(tens), ctypes.byref(hp), cpu_sim.addr(ws), need, None), f"muon_step {wl.name}")
+    sim.ok(lib.muon_step(arr, n, ctypes.byref(hp), cpu_sim.addr(ws), need, None), what)
     st = ctypes.c_int32(-1)
     sim.ok(lib.ma_muon_step_status(cpu_sim.addr(ws), ctypes.byref(st), None), "status")
     assert st.value == 0, ("status word", st.value)
+    return infos, ws
+
+
+def muon_step(sim, wl, tol_ns, update_tol=None, only=None, data=None, hp=None, clip=1.0, h_extra=None):
+    """One step of workload `wl` (or of `data`); every matrix against the
+    oracle's chain: momentum at 1e-5, the Newton-Schulz output (localized
+    bars at tol_ns), NorMuon's V (twice tol_ns) and the stored parameters.
+    `clip`: the factor the gradient is read with (hp.clip then points at
+    the state); `h_extra`: oracle settings beyond the workload's (a
+    coefficient table)."""
+    h = dict(hp_dict(wl.muon_hp), **(h_extra or {}))
+    data = data or workloads.generate(wl, device="cpu", gen_device="cpu", only=only)
+    tens = [t for t in data.muon if t is not None]
+    arr, bufs = load_muon(sim, tens)
+    before = [(P.copy(), M.copy(), None if V is None else V.copy()) for P, _, M, V in bufs]
+    infos, ws = run_muon(sim, arr, len(tens), hp or hp_c(wl.muon_hp), f"muon_step {wl.name}")
     es = 2 if wl.muon_hp.ns_dtype == "bf16" else 4
     for kk, info in enumerate(infos):
         ti = info["tensor"]
@@ -334,7 +351,7 @@ def muon_step(sim, wl, tol_ns, update_tol=None, only=None):
         m, n, bi, v = info["m"], info["n"], info["batch_index"], info["view"]
         rs = slice(v * m, (v + 1) * m)
         W0 = dec(before[ti][0][bi, rs], spec.param_dtype)
-        Gm = dec(G[bi, rs], spec.grad_dtype)
+        Gm = dec(G[bi, rs], spec.grad_dtype) * clip
         B0 = dec(before[ti][1][bi, rs], "f32")
         V0 = None if V is None else dec(before[ti][2][bi, rs], "f32")
         B1 = omuon.momentum_ema(B0, Gm, h["beta"])
@@ -355,7 +372,7 @@ def muon_step(sim, wl, tol_ns, update_tol=None, only=None):
         tol_p = update_tol or (2 if spec.param_dtype == "f32" else 3) * tol_ns
         check_update(dec(P[bi, rs], spec.param_dtype), W0, W_want, Gm, U_dir, h, spec.lr, spec.wd,
                      omuon.shape_scale(m, n), spec.param_dtype, tol_p, tol_ns)
-    return infos
+    return infos, ws, bufs
 
 
 def aspect2_workload(name, seed, **hp):
@@ -423,6 +440,183 @@ def case_moe_mini(sim):
 
 def case_wide_mini(sim):
     muon_step(sim, minis()["wide"], 2e-2)
+
+
+def adamw_call(sim, ts, step, clip_state=None, cautious=False, seed=0, betas=(0.9, 0.999)):
+    """adamw_step on guarded copies of the oracle-format tensors `ts`;
+    returns the buffers (P, G, M, V) per tensor."""
+    arr = (ma.AdamWTensorC * len(ts))()
+    bufs = []
+    for i, t in enumerate(ts):
+        P, G, M, V = (sim.put(t[k]) for k in ("param", "grad", "m", "v"))
+        bufs.append((P, G, M, V))
+        d = arr[i]
+        d.param, d.grad, d.m, d.v = (cpu_sim.addr(x) for x in (P, G, M, V))
+        d.numel = P.size
+        d.param_dtype, d.grad_dtype, d.moment_dtype = (DT[t[k]] for k in ("param_dtype", "grad_dtype", "moment_dtype"))
+        d.lr, d.weight_decay = t["lr"], t["wd"]
+    hp = ma.AdamWHParamsC(betas[0], betas[1], 1e-8, step)
+    hp.cautious = ma.CAUTIOUS["wrapper"] if cautious else 0
+    hp.seed = seed
+    hp.clip = None if clip_state is None else cpu_sim.addr(clip_state)
+    sim.ok(sim.lib.adamw_step(arr, len(ts), ctypes.byref(hp), None), "adamw")
+    return bufs
+
+
+def adam_tensor(n, seed):
+    r = np.random.default_rng(seed)
+    return {"param": storage.round_f32(r.standard_normal(n) * 0.02), "param_dtype": "f32",
+            "grad": storage.round_f32(r.standard_normal(n) * 1e-3), "grad_dtype": "f32",
+            "m": storage.round_f32(r.standard_normal(n) * 1e-4),
+            "v": storage.round_f32(np.abs(r.standard_normal(n)) * 1e-6 + 1e-8), "moment_dtype": "f32",
+            "lr": 1e-3, "wd": 0.1}
+
+
+def case_clip_and_skip(sim):
+    """max_norm a quarter of the norm: Muon (fp32 Newton-Schulz) and AdamW
+    read the gradient times the clip factor, within 1e-5 / 1e-6 of the
+    oracle's clipped step. A non-finite gradient: the state says skip, and
+    every Muon and AdamW buffer keeps its bits."""
+    wl = aspect2_workload("clip", 33, ns_dtype="f32")
+    data = workloads.generate(wl, device="cpu", gen_device="cpu")
+    adam = [adam_tensor(70000, 70)]
+    grads = [(workloads.to_numpy(t.grad), t.spec.grad_dtype) for t in data.muon] + [(adam[0]["grad"], "f32")]
+    norm = ognorm.global_norm(grads)
+    state = grad_norm(sim, grads, norm / 4)
+    cf, skip = ognorm.clip_state(norm, norm / 4)
+    assert not skip and abs(state[1] - cf) <= 1e-6 * cf
+    hp = hp_c(wl.muon_hp)
+    hp.clip = cpu_sim.addr(state)
+    muon_step(sim, wl, 1e-5, update_tol=1e-5, data=data, hp=hp, clip=float(state[1]))
+    (P, G, M, V), = adamw_call(sim, adam, 1, clip_state=state)
+    w = oadamw.adamw_step(adam, {"beta1": 0.9, "beta2": 0.999, "eps": 1e-8, "step": 1}, clip=(float(state[1]), False))[0]
+    assert rel(dec(P, "f32"), w["p64"]) < 1e-6 and rel(dec(M, "f32"), w["m64"]) < 1e-6
+
+    specs = (workloads.MuonTensorSpec("a", 1, 300, 200), workloads.MuonTensorSpec("b", 2, 192, 160, views=2))
+    wl = workloads.Workload("skip", 31, specs, (), workloads.MuonHParams(ns_dtype="bf16", normuon=True,
+                                                                          cautious="wd_mask"))
+    for bad in (np.inf, np.nan):
+        data = workloads.generate(wl, device="cpu", gen_device="cpu")
+        data.muon[1].grad[0, 5, 7] = float(bad)
+        grads = [(workloads.to_numpy(t.grad), "f32") for t in data.muon] + [(adam[0]["grad"], "f32")]
+        state = grad_norm(sim, grads, 1.0)
+        assert state[2] == 1.0, state
+        arr, bufs = load_muon(sim, data.muon)
+        before = [[None if x is None else x.copy() for x in b] for b in bufs]
+        hp = hp_c(wl.muon_hp)
+        hp.clip = cpu_sim.addr(state)
+        run_muon(sim, arr, len(data.muon), hp, "skipped muon_step")
+        abuf = adamw_call(sim, adam, 1, clip_state=state)
+        for b0, b1 in zip(before, bufs):
+            for x0, x1 in zip(b0, b1):
+                assert x0 is None or np.array_equal(x0.view(np.uint8), x1.view(np.uint8)), bad
+        for x0, k in zip(abuf[0], ("param", "grad", "m", "v")):
+            assert np.array_equal(x0, adam[0][k]), (bad, k)
+
+
+NS_TABLE = [(3.4445, -4.7750, 2.0315), (3.1, -4.1, 1.8), (2.9, -3.6, 1.5), (2.4, -2.6, 1.0), (1.875, -1.25, 0.375)]
+
+
+def case_ns_table(sim):
+    """A different (a, b, c) per iteration and the 1.01 normalisation factor,
+    against the oracle with the same table (bf16: 2e-2, fp32 on a matrix of
+    aspect >= 2: 1e-5); a table of five equal rows gives the same bits as
+    none; with a table the persistent launch and the per-launch schedule
+    agree bit for bit."""
+    for dt, shape, tol in (("bf16", (2, 256, 640), 2e-2), ("f32", (64, 300), 1e-5)):
+        rnd = storage.round_bf16_bits if dt == "bf16" else storage.round_f32
+        x = rnd(randn(shape, 90))
+        out = newton_schulz(sim, x, dt, ma.muon_hparams(ns_dtype=dt, ns_table=NS_TABLE, ns_norm_scale=1.01))
+        xs, os_ = (x, out) if x.ndim == 3 else (x[None], out[None])
+        for b in range(xs.shape[0]):
+            check_local(dec(os_[b], dt), omuon.newton_schulz(dec(xs[b], dt), table=NS_TABLE, norm_scale=1.01),
+                        tol, (dt, b))
+        plain = newton_schulz(sim, x, dt).copy()
+        const = newton_schulz(sim, x, dt, ma.muon_hparams(ns_dtype=dt, ns_table=[omuon.NS_COEFFS] * 5))
+        assert np.array_equal(plain, const), dt
+    x = storage.round_bf16_bits(randn((2, 384, 768), 91))
+    hp = ma.muon_hparams(ns_dtype="bf16", ns_table=NS_TABLE)
+    outs = []
+    for sched in ("launches", "persistent"):
+        os.environ["MA_NS_SCHEDULE"] = sched
+        try:
+            outs.append(newton_schulz(sim, x, "bf16", hp).copy())
+        finally:
+            del os.environ["MA_NS_SCHEDULE"]
+    assert np.array_equal(outs[0], outs[1])
+    # the whole step with a table: Newton-Schulz inside muon_step follows it
+    wl = aspect2_workload("table", 43, ns_dtype="f32")
+    hp = ma.muon_hparams(ns_dtype="f32", ns_table=NS_TABLE, ns_norm_scale=1.01)
+    muon_step(sim, wl, 1e-5, update_tol=1e-5, hp=hp, h_extra={"ns_table": NS_TABLE, "ns_norm_scale": 1.01})
+
+
+def case_state_and_views(sim):
+    """Two steps, each side continuing from its own stored state (fp32
+    Newton-Schulz: parameters within 1e-5); Nesterov off; an absent gradient
+    leaves its tensor alone and a zero gradient only decays it; a packed
+    tensor of two views steps exactly like its halves passed separately."""
+    wl = aspect2_workload("two_steps", 21, ns_dtype="f32")
+    data = workloads.generate(wl, device="cpu", gen_device="cpu")
+    h = hp_dict(wl.muon_hp)
+    inp = [{"param": workloads.to_numpy(t.param), "param_dtype": "f32", "grad": workloads.to_numpy(t.grad),
+            "grad_dtype": "f32", "momentum": workloads.to_numpy(t.momentum), "row_v": None, "views": t.spec.views,
+            "lr": t.spec.lr, "wd": t.spec.wd, "shape": t.spec.shape} for t in data.muon]
+    arr, bufs = load_muon(sim, data.muon)
+    hp = hp_c(wl.muon_hp)
+    run_muon(sim, arr, len(data.muon), hp, "step 1")
+    want1 = omuon.muon_step(inp, h)
+    r = np.random.default_rng(99)
+    for (P, G, M, V) in bufs:
+        G[...] = storage.round_f32(r.standard_normal(G.shape))
+    inp2 = [dict(i, param=w["param"], momentum=w["momentum"], grad=b[1].copy()) for i, w, b in zip(inp, want1, bufs)]
+    run_muon(sim, arr, len(data.muon), hp, "step 2")
+    for b, w in zip(bufs, omuon.muon_step(inp2, h)):
+        assert rel(dec(b[0], "f32"), w["W64"]) < 1e-5
+        check_local(dec(b[2], "f32").reshape(w["B64"].shape), w["B64"], 1e-5, "momentum, step 2")
+
+    muon_step(sim, aspect2_workload("plain_momentum", 22, ns_dtype="f32", nesterov=False), 1e-5, update_tol=1e-5)
+
+    data = workloads.generate(aspect2_workload("absent_zero", 23), device="cpu", gen_device="cpu")
+    data.muon[1].grad = None
+    data.muon[2].grad = data.muon[2].grad * 0
+    arr, bufs = load_muon(sim, data.muon)
+    keep = [(b[0].copy(), b[2].copy()) for b in bufs]
+    run_muon(sim, arr, len(data.muon), hp_c(data.workload.muon_hp), "absent and zero gradients")
+    assert np.array_equal(bufs[1][0], keep[1][0]) and np.array_equal(bufs[1][2], keep[1][1])
+    decay = np.float32(1.0 - np.float64(np.float32(0.02)) * np.float64(np.float32(0.1)))
+    assert np.array_equal(bufs[2][0], keep[2][0] * decay) and not bufs[2][2].any()
+    assert not np.array_equal(bufs[0][0], keep[0][0])
+
+    S = workloads.MuonTensorSpec
+    packed = workloads.Workload("packed", 3, (S("p", 1, 2 * 96, 160, views=2),), (), workloads.MuonHParams())
+    d1 = workloads.generate(packed, device="cpu", gen_device="cpu")
+    t = d1.muon[0]
+    halves = workloads.WorkloadData(packed, [
+        workloads.MuonTensorData(S("h0", 1, 96, 160), t.param[:, :96].contiguous(), t.grad[:, :96].contiguous(),
+                                 t.momentum[:, :96].contiguous(), None),
+        workloads.MuonTensorData(S("h1", 1, 96, 160), t.param[:, 96:].contiguous(), t.grad[:, 96:].contiguous(),
+                                 t.momentum[:, 96:].contiguous(), None)], [])
+    a1, b1 = load_muon(sim, d1.muon)
+    a2, b2 = load_muon(sim, halves.muon)
+    run_muon(sim, a1, 1, hp_c(packed.muon_hp), "packed")
+    run_muon(sim, a2, 2, hp_c(packed.muon_hp), "halves")
+    assert np.array_equal(b1[0][0][:, :96], b2[0][0]) and np.array_equal(b1[0][0][:, 96:], b2[1][0])
+    assert np.array_equal(b1[0][2][:, :96], b2[0][2])
+
+
+def case_symmetric_products(sim):
+    """A = s X X^T and B = bA + cA^2 are stored with equal triangles, bit for
+    bit, after a bf16 step (SQUARE and APPLY may read them along either
+    index): every matrix's last A and B."""
+    wl = aspect2_workload("symmetric", 44, ns_dtype="bf16")
+    infos, ws, _ = muon_step(sim, wl, 2e-2)
+    for kk, info in enumerate(infos):
+        rp = info["rp"]
+        for nm in ("a_offset", "b_offset"):
+            o = info[nm]
+            Mx = ws[o:o + rp * rp * 2].view(np.uint16).reshape(rp, rp)
+            assert np.array_equal(Mx, Mx.T), (kk, nm, int((Mx != Mx.T).sum()))
+            assert Mx.any(), (kk, nm)
 
 
 def case_single_256x128(sim):

@@ -20,6 +20,11 @@ bars:
 - the status word when some XCD's queue gets no workgroup;
 - the matrix-core ceiling loop against its closed form;
 - whole Muon steps with every epilogue;
+- the global-norm clip (both halves read the clipped gradient) and skip
+  (every buffer keeps its bits); a per-iteration coefficient table with the
+  1.01 normalisation factor; two steps continuing from stored state;
+  Nesterov off; absent and zero gradients; packed views against their halves;
+  A and B stored symmetric bit for bit;
 - layer 0 of the GPT workload at its real shapes, and small copies of the
   Llama, MoE and wide workloads (their dtypes, views, batches, outliers and
   epilogues).
@@ -170,6 +175,8 @@ CASES = [
     ("muon_bf16", ()), ("muon_bf16", ("--schedule", "waves-down", "--mode", "head")),
     ("gpt_layer0", ()), ("llama_mini", ("--schedule", "waves-up")), ("moe_mini", ("--mode", "head")),
     ("wide_mini", ("--schedule", "waves-down")),
+    ("clip_and_skip", ("--mode", "head")), ("ns_table", ("--schedule", "waves-up")), ("state_and_views", ()),
+    ("symmetric_products", ("--schedule", "waves-down")),
 ]
 
 
@@ -184,7 +191,7 @@ def case_results():
     current; each test waits for its own."""
     simbuild.build()
     ex = ThreadPoolExecutor(4)
-    slow_first = sorted(CASES, key=lambda ca: ca[0] not in ("wide_mini", "gpt_layer0", "ns_layouts", "ns_schedules"))
+    slow_first = sorted(CASES, key=lambda ca: ca[0] not in ("gpt_layer0", "ns_table", "ns_layouts", "ns_schedules"))
     futs = {(c, a): ex.submit(_run, c, a) for c, a in slow_first}
     yield futs
     ex.shutdown(wait=True)
