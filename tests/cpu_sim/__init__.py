@@ -57,11 +57,15 @@ class Arena:
 
     ``mode="tail"``: the buffer ends 0-15 bytes before an inaccessible page
     (the start stays 16-byte aligned, as the kernels' vector accesses need).
-    ``mode="head"``: it starts right after one (page-aligned)."""
+    ``mode="head"``: it starts right after one (page-aligned).
+    ``poison``: every buffer starts as 0xFF bytes (NaN as fp32 or bf16), so
+    workspaces and outputs hold garbage on entry, as callers may pass them;
+    inputs are copied over it (``like``)."""
 
-    def __init__(self, mode: str = "tail"):
+    def __init__(self, mode: str = "tail", poison: bool = False):
         assert mode in ("tail", "head")
         self.mode = mode
+        self.poison = poison
         self._maps = []
 
     def bytes(self, nbytes: int) -> np.ndarray:
@@ -78,7 +82,10 @@ class Arena:
         else:
             start = (PAGE + body - nbytes) // 16 * 16
         self._maps.append(m)
-        return np.frombuffer(m, dtype=np.uint8, count=nbytes, offset=start)
+        out = np.frombuffer(m, dtype=np.uint8, count=nbytes, offset=start)
+        if self.poison:
+            out[...] = 0xFF      # NaN in fp32 and bf16: a read of anything not written shows
+        return out
 
     def array(self, shape, dtype) -> np.ndarray:
         dt = np.dtype(dtype)

@@ -5,7 +5,11 @@ inputs in guarded buffers and compares every output with the fp64 oracle, at
 the bars the GPU parity tests use. One case per child process:
 
     python -m tests.cpu_sim.cases <case> [--mode tail|head] [--workers N] [--immediate-dma] [--lib PATH]
-        [--schedule together|waves-up|waves-down]
+        [--schedule together|waves-up|waves-down] [--no-poison]
+
+Workspaces and outputs start as 0xFF bytes (NaN in both float formats): the
+header promises that a workspace's contents on entry do not matter, and
+fresh zeroed memory would hide a read of padding the library never wrote.
 
 Exit status 0: passed. 1: a mismatch or a simulator fault (message on
 stderr). Killed by SIGSEGV: an access outside a buffer hit a guard page.
@@ -37,12 +41,12 @@ DT = {"f32": ma.MA_F32, "bf16": ma.MA_BF16}
 
 
 class Sim:
-    def __init__(self, mode="tail", workers=8, deferred=True, lib=None, schedule=0):
+    def __init__(self, mode="tail", workers=8, deferred=True, lib=None, schedule=0, poison=False):
         self.lib = cpu_sim.load(lib or cpu_sim.LIB)
         self.lib.hipsim_set_schedule(schedule)
         self.lib.hipsim_set_workers(workers)
         self.lib.hipsim_set_dma_deferred(1 if deferred else 0)
-        self.arena = cpu_sim.Arena(mode)
+        self.arena = cpu_sim.Arena(mode, poison)
 
     def ok(self, status, what=""):
         fault = self.lib.hipsim_fault().decode()
@@ -635,8 +639,10 @@ def main(argv=None):
     ap.add_argument("--immediate-dma", action="store_true")
     ap.add_argument("--lib", default=None, help="another simulator build of the sources")
     ap.add_argument("--schedule", default="together", choices=SCHEDULES)
+    ap.add_argument("--no-poison", action="store_true",
+                    help="workspaces and outputs start zeroed instead of as NaN bytes")
     a = ap.parse_args(argv)
-    sim = Sim(a.mode, a.workers, not a.immediate_dma, a.lib, SCHEDULES.index(a.schedule))
+    sim = Sim(a.mode, a.workers, not a.immediate_dma, a.lib, SCHEDULES.index(a.schedule), not a.no_poison)
     try:
         CASES[a.case](sim)
     except AssertionError:

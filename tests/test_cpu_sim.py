@@ -28,8 +28,10 @@ bars:
 - layer 0 of the GPT workload at its real shapes, and small copies of the
   Llama, MoE and wide workloads (their dtypes, views, batches, outliers and
   epilogues).
-The cases run under the three lane schedules and with guard pages before
-and after the buffers.
+The cases run under the three lane schedules, with guard pages before and
+after the buffers, and with every workspace and output filled with NaN
+bytes on entry (fresh zeroed memory would hide a read of padding the library
+never wrote).
 
 This checks the sources' arithmetic, indexing and synchronisation as
 written. It does not check the GPU's timing, caches or compiler. A CPU
