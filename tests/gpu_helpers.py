@@ -130,10 +130,15 @@ def check_update(W_gpu, W0, W_want, G, U_dir, h, lr, wd, s, param_dtype, tol, to
     A cautious mask is a decision on the update direction, which the two
     sides compute to different precision: an element may take the other
     branch only where the oracle's own margin is inside the direction's
-    element bar (6 tol_ns of the RMS update), and then it equals that branch
-    (both branches rounded to the parameter dtype; where they round alike
-    there is nothing to tell). At most 3% of elements flip with bf16
-    Newton-Schulz, 0.1% with fp32.
+    element bar (6 tol_ns of the RMS update), and then it is compared with
+    the branch it is closer to (both branches rounded to the parameter
+    dtype). Inside that band the two branches often differ by less than the
+    update's element bar (the weight-decay mask moves an element by lr wd W
+    only), so being closer to the other branch says nothing. A flip counts
+    where the value is outside the element bar of the expected branch: at
+    most 3% of elements with bf16 Newton-Schulz, 0.1% with fp32. The kernel
+    sources on the CPU simulator put 1.2-4.6% of elements closer to the
+    other branch on the small mixed shapes and flip none.
 
     fp32 parameters: the update W - W0 within `tol` of the oracle's, under
     the localized bars. bf16 parameters: every element within one bf16
@@ -156,11 +161,16 @@ def check_update(W_gpu, W0, W_want, G, U_dir, h, lr, wd, s, param_dtype, tol, to
         alt, near = W_want, np.zeros(W_want.shape, dtype=bool)
     rounded = lambda x: storage.decode(storage.round_to(x, param_dtype), param_dtype)
     R_want, R_alt = rounded(W_want), rounded(alt)
-    flipped = near & (np.abs(W_gpu - R_alt) < np.abs(W_gpu - R_want))
+    closer = near & (np.abs(W_gpu - R_alt) < np.abs(W_gpu - R_want))
+    dW0 = W_want - W0
+    bar = 6 * tol * (np.sqrt(np.mean(dW0 * dW0)) + np.abs(dW0))
+    if param_dtype == "bf16":
+        bar = bar + bf16_spacing(R_want)
+    flipped = closer & (np.abs(W_gpu - R_want) > bar)
     loose = tol_ns > 1e-3
     assert flipped.mean() <= (0.03 if loose else 1e-3), ("mask flips", float(flipped.mean()))
-    exact = np.where(flipped, alt, W_want)
-    W_ref = np.where(flipped, R_alt, R_want)
+    exact = np.where(closer, alt, W_want)
+    W_ref = np.where(closer, R_alt, R_want)
     if param_dtype == "bf16":
         dW = exact - W0
         allowed = bf16_spacing(W_ref) + 6 * tol * (np.sqrt(np.mean(dW * dW)) + np.abs(dW))

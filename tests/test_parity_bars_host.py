@@ -99,3 +99,62 @@ def test_ulp_distance():
     assert bf16_ulps([0x0000], [0x8000]).tolist() == [0]          # +0 and -0
     assert bf16_ulps([0x0001], [0x8001]).tolist() == [2]          # across zero
     assert bf16_ulps([0xBF80], [0xBF82]).tolist() == [2]
+
+
+# ---------------------------------------------------------------------------
+# check_update: the cautious masks
+# ---------------------------------------------------------------------------
+def _update_case(cautious, param_dtype="f32", seed=12):
+    """A 300 x 200 step: the oracle's result, the same step taken with the
+    bf16 chain's U and with U to fp32 precision (relative noise 1e-7)."""
+    from oracle import storage
+    r = np.random.default_rng(seed)
+    m, n, lr, wd = 300, 200, 0.02, 0.1
+    W0 = storage.decode(storage.round_to(r.standard_normal((m, n)) * 0.02, param_dtype), param_dtype)
+    G = r.standard_normal((m, n)) * 1e-3
+    Q = bf16(G.astype(np.float32)).astype(np.float64)
+    U, U_chain = omuon.newton_schulz(Q), ns_bf16_chain(Q)
+    U_f32 = U * (1.0 + 1e-7 * r.standard_normal(U.shape))
+    s = omuon.shape_scale(m, n)
+
+    def step(Ud):
+        if cautious == "wd_mask":
+            return omuon.apply_cautious_wd(W0, Ud, lr, wd, s)
+        return omuon.apply_cautious_wrapper(W0, Ud, G, lr, wd, s)[0]
+
+    rnd = lambda x: storage.decode(storage.round_to(x, param_dtype), param_dtype)
+    return dict(W0=W0, G=G, U=U, h={"cautious": cautious}, lr=lr, wd=wd, s=s, want=step(U), chain=rnd(step(U_chain)),
+                near_exact=rnd(step(U_f32)), rnd=rnd)
+
+
+@pytest.mark.parametrize("cautious,pd", [("wd_mask", "f32"), ("wd_mask", "bf16"), ("wrapper", "f32"),
+                                         ("wrapper", "bf16")])
+def test_update_check_admits_the_bf16_chain_and_rejects_mask_mistakes(cautious, pd):
+    """At the bf16 Newton-Schulz bars the step taken with the bf16 chain's
+    update passes. At the fp32 bars (1e-5) the step taken with U to fp32
+    precision passes, and the same step with the mask inverted, with no mask,
+    or with 5% of the decisions turned over fails. (At the bf16 bars the
+    weight-decay mask is not visible: it moves an element by lr wd W, about
+    3% of the update's RMS here, as much as a 2e-2 error of U moves it.)"""
+    from tests.gpu_helpers import check_update
+    c = _update_case(cautious, pd)
+    W0, U, G, lr, wd, s = c["W0"], c["U"], c["G"], c["lr"], c["wd"], c["s"]
+    common = (W0, c["want"], G, U, c["h"], lr, wd, s, pd)
+    check_update(c["chain"], *common, 6e-2 if pd == "bf16" else 4e-2, 2e-2)
+    check_update(c["near_exact"], *common, 1e-5, 1e-5)
+    # the other branch everywhere: decay where U W < 0 (the mask keeps it where
+    # U W >= 0); the update where it opposes the gradient (the wrapper keeps
+    # it where (W - W_new) G > 0)
+    if cautious == "wd_mask":
+        inverted = W0 - lr * s * U - lr * wd * np.where((U * W0) >= 0.0, 0.0, W0)
+    else:
+        delta = lr * wd * W0 + lr * s * U
+        inverted = np.where((delta * G) > 0.0, W0, W0 - delta)
+    plain = omuon.apply_decoupled(W0, U, lr, wd, s)
+    turned = c["want"].copy()
+    pick = np.random.default_rng(3).random(turned.shape) < 0.05
+    turned[pick] = inverted[pick]
+    for name, bad in (("inverted", inverted), ("no mask", plain), ("5% turned", turned)):
+        with pytest.raises(AssertionError):
+            check_update(c["rnd"](bad), *common, 1e-5, 1e-5)
+            pytest.fail(f"{name} passed")
