@@ -33,6 +33,10 @@ after the buffers, and with every workspace and output filled with NaN
 bytes on entry (fresh zeroed memory would hide a read of padding the library
 never wrote).
 
+Last, the smaller tests of the GPU test files themselves run on CPU tensors
+against the simulator build (``tests/cpu_sim/gpu_plugin.py``), so their own
+logic and bars are checked against the kernels as written.
+
 This checks the sources' arithmetic, indexing and synchronisation as
 written. It does not check the GPU's timing, caches or compiler. A CPU
 build stands in for the hardware; the GPU tests are the parity tests proper.
@@ -182,21 +186,45 @@ CASES = [
 ]
 
 
+# The GPU test files themselves, on CPU tensors against the simulator build
+# (tests/cpu_sim/gpu_plugin.py): the smaller tests of each file.
+GPU_FILES = [
+    ("tests/test_gpu_next_rows.py", "not slow"),
+    ("tests/test_gpu_parity.py", "f32 or small or absent or views or two_steps or zero or transpose or "
+                                 "1x1 or 7x3 or 300x200 or 200x300"),
+    ("tests/test_gpu_strict.py", "f32_local or epilogues or single or range_ends or huge"),
+]
+
+
 def _run(case, args):
     cmd = [sys.executable, "-m", "tests.cpu_sim.cases", case, *args]
     return subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=1200)
 
 
+def _run_gpu_file(path, expr):
+    cmd = [sys.executable, "-m", "pytest", path, "-m", "gpu", "-p", "tests.cpu_sim.gpu_plugin", "-q",
+           "-p", "no:cacheprovider", "-k", expr]
+    return subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=1200)
+
+
 @pytest.fixture(scope="module")
 def case_results():
-    """All cases start at once, four at a time, once the simulator build is
-    current; each test waits for its own."""
+    """All cases and GPU-file runs start at once, four at a time, once the
+    simulator build is current; each test waits for its own."""
     simbuild.build()
     ex = ThreadPoolExecutor(4)
+    futs = {("gpu-file", p): ex.submit(_run_gpu_file, p, e) for p, e in GPU_FILES}
     slow_first = sorted(CASES, key=lambda ca: ca[0] not in ("gpt_layer0", "ns_table", "ns_layouts", "ns_schedules"))
-    futs = {(c, a): ex.submit(_run, c, a) for c, a in slow_first}
+    futs.update({(c, a): ex.submit(_run, c, a) for c, a in slow_first})
     yield futs
     ex.shutdown(wait=True)
+
+
+@pytest.mark.parametrize("path", [p for p, _ in GPU_FILES])
+def test_gpu_test_files_pass_on_the_simulator(case_results, path):
+    r = case_results[("gpu-file", path)].result()
+    assert r.returncode == 0, f"{path}:\n{r.stdout[-4000:]}\n{r.stderr[-2000:]}"
+    assert " passed" in r.stdout and "failed" not in r.stdout, r.stdout[-2000:]
 
 
 @pytest.mark.parametrize("case,args", CASES, ids=[c + ("-" + "-".join(a[1::2]) if a else "") for c, a in CASES])
