@@ -69,8 +69,8 @@ def pytest_configure(config):
 def pytest_collection_modifyitems(session, config, items):
     import tests.gpu_helpers as gh
     for name, mod in list(sys.modules.items()):
-        if name.startswith(("tests.test_gpu", "test_gpu")):
-            if hasattr(mod, "DEV"):
+        if name.startswith("tests.") or name.startswith(("test_", "wip_")):
+            if getattr(mod, "DEV", None) == "cuda":
                 mod.DEV = "cpu"
             if hasattr(mod, "to_gpu"):
                 mod.to_gpu = gh.to_gpu
