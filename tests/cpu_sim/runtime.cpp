@@ -636,7 +636,14 @@ int hipsim_set_workers(int n) {
 int hipsim_set_dma_deferred(int on) { return hipsim::g_defer_dma.exchange(on != 0) ? 1 : 0; }
 int hipsim_set_xcds(int n) { return hipsim::g_xcds.exchange(n < 1 || n > 8 ? 8 : n); }
 int hipsim_set_schedule(int policy) { return hipsim::g_schedule.exchange(policy < 0 || policy > 2 ? 0 : policy); }
-const char* hipsim_fault() { return hipsim::g_fault.c_str(); }
+// The first fault since the last clear ("" if none): a copy taken under the
+// lock, valid until this thread's next call.
+const char* hipsim_fault() {
+  static thread_local std::string copy;
+  std::lock_guard<std::mutex> lk(hipsim::g_mu);
+  copy = hipsim::g_fault;
+  return copy.c_str();
+}
 void hipsim_clear_fault() {
   std::lock_guard<std::mutex> lk(hipsim::g_mu);
   hipsim::g_fault.clear();
