@@ -171,7 +171,9 @@ def _command(src_path: str, obj: str, gen_dir: str) -> list[str]:
             "-o", obj]
 
 
-def build(csrc: str = CSRC, out: str = LIB, verbose: bool = False) -> str:
+def build(csrc: str = CSRC, out: str = LIB, verbose: bool = False, extra=()) -> str:
+    """``extra``: more compiler flags for every object and the link (a
+    sanitizer, say)."""
     os.makedirs(BUILD, exist_ok=True)
     tag = os.path.splitext(os.path.basename(out))[0]
     objdir = os.path.join(BUILD, tag + "_obj")
@@ -180,10 +182,10 @@ def build(csrc: str = CSRC, out: str = LIB, verbose: bool = False) -> str:
     for s in SOURCES:
         obj = os.path.join(objdir, os.path.splitext(s)[0] + ".o")
         cmd = _command(os.path.join(csrc, s), obj, objdir)
-        cmd[cmd.index("-c"):cmd.index("-c")] = ["-I", csrc]
+        cmd[cmd.index("-c"):cmd.index("-c")] = ["-I", csrc, *extra]
         jobs.append((s, cmd, obj))
     rt_obj = os.path.join(objdir, "runtime.o")
-    jobs.append(("runtime.cpp", [CXX, *FLAGS, "-I", os.path.join(HERE, "include"), "-c",
+    jobs.append(("runtime.cpp", [CXX, *FLAGS, *extra, "-I", os.path.join(HERE, "include"), "-c",
                                  os.path.join(HERE, "runtime.cpp"), "-o", rt_obj], rt_obj))
 
     def run(job):
@@ -197,7 +199,7 @@ def build(csrc: str = CSRC, out: str = LIB, verbose: bool = False) -> str:
     with ThreadPoolExecutor(min(len(jobs), int(os.environ.get("MAX_JOBS", "8")))) as ex:
         list(ex.map(run, jobs))
     tmp = out + ".tmp"
-    r = subprocess.run([CXX, "-shared", "-pthread", "-o", tmp, *[o for _, _, o in jobs]],
+    r = subprocess.run([CXX, "-shared", "-pthread", *extra, "-o", tmp, *[o for _, _, o in jobs]],
                        capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError("simulator link failed:\n" + r.stdout + r.stderr)
@@ -225,5 +227,8 @@ if __name__ == "__main__":
     ap = argparse.ArgumentParser()
     ap.add_argument("--csrc", default=CSRC)
     ap.add_argument("--out", default=LIB)
+    ap.add_argument("--ubsan", action="store_true",
+                    help="with UndefinedBehaviorSanitizer (load with its runtime preloaded)")
     a = ap.parse_args()
-    print(build(a.csrc, a.out, verbose=True))
+    extra = ("-fsanitize=undefined", "-fno-sanitize-recover=undefined", "-shared-libsan") if a.ubsan else ()
+    print(build(a.csrc, a.out, verbose=True, extra=extra))

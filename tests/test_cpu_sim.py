@@ -33,6 +33,10 @@ after the buffers, and with every workspace and output filled with NaN
 bytes on entry (fresh zeroed memory would hide a read of padding the library
 never wrote).
 
+A few cases also run on a build with UndefinedBehaviorSanitizer: signed
+overflow in the kernels' index arithmetic, a misaligned vector access or a
+bad shift stops them.
+
 Last, the smaller tests of the GPU test files themselves run on CPU tensors
 against the simulator build (``tests/cpu_sim/gpu_plugin.py``), so their own
 logic and bars are checked against the kernels as written.
@@ -196,9 +200,27 @@ GPU_FILES = [
 ]
 
 
-def _run(case, args):
+# Cases on a build with UndefinedBehaviorSanitizer: signed overflow in the
+# kernels' index arithmetic, misaligned vector accesses, bad shifts abort.
+UBSAN_CASES = [("adamw", ()), ("grad_norm", ()), ("ns_f32", ()), ("muon_bf16", ("--schedule", "waves-up")),
+               ("state_and_views", ())]
+UBSAN_LIB = os.path.join(simbuild.BUILD, "libmuon_adamw_sim_ubsan.so")
+
+
+def _ubsan_runtime():
+    import glob
+    found = glob.glob(os.path.join(os.path.dirname(simbuild.CXX), "..", "lib", "clang", "*", "lib", "linux",
+                                   "libclang_rt.ubsan_standalone-x86_64.so"))
+    return found[0] if found else None
+
+
+def _run(case, args, ubsan=False):
     cmd = [sys.executable, "-m", "tests.cpu_sim.cases", case, *args]
-    return subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=1200)
+    env = None
+    if ubsan:
+        cmd += ["--lib", UBSAN_LIB]
+        env = dict(os.environ, LD_PRELOAD=_ubsan_runtime(), UBSAN_OPTIONS="print_stacktrace=1")
+    return subprocess.run(cmd, cwd=ROOT, capture_output=True, text=True, timeout=1200, env=env)
 
 
 def _run_gpu_file(path, expr):
@@ -212,10 +234,16 @@ def case_results():
     """All cases and GPU-file runs start at once, four at a time, once the
     simulator build is current; each test waits for its own."""
     simbuild.build()
+    have_ubsan = _ubsan_runtime() is not None
+    if have_ubsan:
+        simbuild.build(out=UBSAN_LIB, extra=("-fsanitize=undefined", "-fno-sanitize-recover=undefined",
+                                             "-shared-libsan"))
     ex = ThreadPoolExecutor(4)
     futs = {("gpu-file", p): ex.submit(_run_gpu_file, p, e) for p, e in GPU_FILES}
     slow_first = sorted(CASES, key=lambda ca: ca[0] not in ("gpt_layer0", "ns_table", "ns_layouts", "ns_schedules"))
     futs.update({(c, a): ex.submit(_run, c, a) for c, a in slow_first})
+    if have_ubsan:
+        futs.update({("ubsan", c, a): ex.submit(_run, c, a, True) for c, a in UBSAN_CASES})
     yield futs
     ex.shutdown(wait=True)
 
@@ -234,3 +262,12 @@ def test_kernels_against_the_oracle(case_results, case, args):
         pytest.fail(f"{case} {args}: killed by signal {-r.returncode} (11: an access hit a guard page)\n{r.stderr}")
     assert r.returncode == 0, f"{case} {args}:\n{r.stdout}\n{r.stderr}"
     assert "ok;" in r.stdout
+
+
+@pytest.mark.parametrize("case,args", UBSAN_CASES, ids=[c + ("-" + "-".join(a[1::2]) if a else "") for c, a in UBSAN_CASES])
+def test_kernels_under_undefined_behaviour_sanitizer(case_results, case, args):
+    if ("ubsan", case, args) not in case_results:
+        pytest.skip("no UndefinedBehaviorSanitizer runtime next to the compiler")
+    r = case_results[("ubsan", case, args)].result()
+    assert r.returncode == 0, f"{case} {args} (UBSan):\n{r.stdout}\n{r.stderr[-4000:]}"
+    assert "ok;" in r.stdout and "runtime error" not in r.stderr
